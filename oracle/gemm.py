@@ -1,0 +1,120 @@
+"""Block-scaled FP8 GEMM — fp64 oracle and comparison rules (test infrastructure).
+
+What the GEMM computes ("How to Profile DeepSeek-V3 Inference Kernels Using
+Triton Autotuning", sections "Understanding the Autotuned Kernels in
+DeepSeek-V3" and "Benchmarking the FP8 GEMM Kernel": a matmul of e4m3 matrices
+with per-block scaling factors ``a_s`` and ``b_s``, K tiled by 128):
+
+    C[m, n] = sum_b  sa[m, b] * sw[n // 128, b] * sum_{k in block b} A[m, k] * W[n, k]
+
+with A [M, K] e4m3 and sa [M, K/128] (1x128 activation blocks), W [N, K] e4m3
+and sw [N/128, K/128] (128x128 weight blocks), C = A . W^T of shape [M, N] and
+bf16 output. Because every scale is constant over its block, this equals the
+plain product of the dequantized operands, which is what the oracle computes,
+in float64: Abar = dec(A) * sa, Wbar = dec(W) * sw, R = Abar @ Wbar^T.
+
+Comparison (a reading; the pages give no GEMM tolerance): the bf16 result C
+must satisfy
+  (i)  normwise: max|C - R| / max|R| <= 1e-2, and
+  (ii) elementwise: |C - R| <= 4 * ulp_bf16(R) + tau * S,
+with S = |Abar| @ |Wbar|^T and tau = (128 + K/128 + 2) * 2**-24, the
+standard first-order bound on fp32 summation of that many terms (Higham,
+"Accuracy and Stability of Numerical Algorithms", ch. 4); the 4 bf16 ulps
+cover the final rounding to bf16 with room for the fp32 partial sums.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import e4m3
+
+BLOCK = 128
+
+
+def dequant_act(qa: np.ndarray, sa: np.ndarray) -> np.ndarray:
+    """dec(A) * sa over 1x128 blocks, float64 [M, K] (each product is exact)."""
+    qa = np.asarray(qa, dtype=np.uint8)
+    M, K = qa.shape
+    sa = np.asarray(sa, dtype=np.float32).astype(np.float64)
+    if sa.shape != (M, K // BLOCK):
+        raise ValueError("activation scale shape must be [M, K/128]")
+    return e4m3.decode(qa) * np.repeat(sa, BLOCK, axis=1)
+
+
+def dequant_weight(qw: np.ndarray, sw: np.ndarray) -> np.ndarray:
+    """dec(W) * sw over 128x128 blocks, float64 [N, K] (each product is exact)."""
+    qw = np.asarray(qw, dtype=np.uint8)
+    N, K = qw.shape
+    sw = np.asarray(sw, dtype=np.float32).astype(np.float64)
+    if sw.shape != (N // BLOCK, K // BLOCK):
+        raise ValueError("weight scale shape must be [N/128, K/128]")
+    full = np.repeat(np.repeat(sw, BLOCK, axis=0), BLOCK, axis=1)
+    return e4m3.decode(qw) * full
+
+
+def gemm_blockscaled_ref(qa, sa, qw, sw) -> np.ndarray:
+    """Reference C = Abar @ Wbar^T in float64, shape [M, N]."""
+    return dequant_act(qa, sa) @ dequant_weight(qw, sw).T
+
+
+def gemm_abs_ref(qa, sa, qw, sw) -> np.ndarray:
+    """S = |Abar| @ |Wbar|^T in float64, the scale of the summation error."""
+    return np.abs(dequant_act(qa, sa)) @ np.abs(dequant_weight(qw, sw)).T
+
+
+def gemm_rows_ref(qa, sa, qw, sw, rows, cols):
+    """Reference values R and S at sampled output positions (rows[i], cols[i]),
+    computed one by one, so that full-size outputs can be checked without the
+    full fp64 product."""
+    A = dequant_act(qa[rows], sa[rows])
+    W = dequant_weight(qw, sw)
+    Wc = W[cols]
+    R = np.einsum("ik,ik->i", A, Wc)
+    S = np.einsum("ik,ik->i", np.abs(A), np.abs(Wc))
+    return R, S
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_rne(v: np.ndarray) -> np.ndarray:
+    """float64 -> bf16 bits, one rounding to nearest, ties to even."""
+    v = np.asarray(v, dtype=np.float64)
+    mant, expo = np.frexp(v)
+    out = np.where(np.abs(v) >= 2.0 ** -126,
+                   np.ldexp(np.rint(mant * 256.0), expo - 8),
+                   np.rint(v * 2.0 ** 133) * 2.0 ** -133)
+    return (out.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def ulp_bf16(r: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |r|: 2**(floor(log2|r|) - 7), at least the
+    subnormal spacing 2**-133."""
+    r = np.abs(np.asarray(r, dtype=np.float64))
+    _, fe = np.frexp(r)
+    u = np.ldexp(1.0, fe - 1 - 7)
+    return np.maximum(u, 2.0 ** -133)
+
+
+def gemm_tolerance_tau(K: int) -> float:
+    return (BLOCK + K // BLOCK + 2) * 2.0 ** -24
+
+
+def compare_gemm(c_bits: np.ndarray, R: np.ndarray, S: np.ndarray, K: int):
+    """Check a bf16 GEMM result against the fp64 reference.
+
+    Returns a dict with the normwise error, the worst elementwise ratio
+    |C-R| / (4 ulp + tau S) and a boolean ``ok``.
+    """
+    C = bf16_bits_to_f64(c_bits)
+    R = np.asarray(R, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    err = np.abs(C - R)
+    rmax = float(np.max(np.abs(R))) if R.size else 0.0
+    normwise = float(np.max(err)) / rmax if rmax > 0 else float(np.max(err, initial=0.0))
+    bound = 4.0 * ulp_bf16(R) + gemm_tolerance_tau(K) * S
+    ratio = float(np.max(err / bound)) if err.size else 0.0
+    return dict(normwise=normwise, elem_ratio=ratio,
+                ok=bool(normwise <= 1e-2 and ratio <= 1.0))

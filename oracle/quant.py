@@ -1,0 +1,101 @@
+"""Dynamic FP8 (e4m3) quantization — oracle (test infrastructure).
+
+Three quantizers, all with the same rule and differing only in the set of
+elements that share one scale:
+
+* ``act_quant_block``: one scale per 1x128 block along the last dimension of a
+  row-major [M, K] activation ("How to Profile DeepSeek-V3 Inference Kernels
+  Using Triton Autotuning", section "Benchmarking the Activation Quantization
+  Kernel": ``act_quant(x, block_size=128)`` returns the e4m3 tensor ``y`` and
+  the per-block scales ``s``; section "Understanding the Autotuned Kernels in
+  DeepSeek-V3": block-wise quantization producing FP8 tensors and per-block
+  scaling factors).
+* ``amax_quant_tensor``: one scale for the whole tensor, from an exact amax
+  over every element (TensorRT-LLM PR "Size the per-tensor FP8 dynamic-quant
+  amax grid to the input", sections "Description" and "Correctness": the amax
+  is an exact reduction and the scale is amax / 448).
+* ``weight_quant_block``: one scale per 128x128 block of a row-major [N, K]
+  weight (the block-scaled weights the FP8 GEMM of the DeepSeek-V3 page takes
+  as ``b_s``; the same rule applied to square blocks).
+
+The rule for a group G of bf16 values x:
+    amax  = max over G of |x|                      (exact)
+    s     = fl32(amax / 448)                       (IEEE fp32 division)
+    q[i]  = e4m3(clamp(fl32(x[i] / s), -448, 448)) (fp32 division, then RNE)
+with the reading that a group with amax = 0 gets s = 0 and all-zero (0x00)
+codes, since x / 0 is undefined and every element of such a group is zero.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import e4m3
+
+F448 = np.float32(448.0)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32)
+
+
+def _quant_groups(xf: np.ndarray):
+    """Quantize a float32 array of shape [G, n]: each row is one group."""
+    amax = np.max(np.abs(xf), axis=1)                 # exact
+    s = (amax / F448).astype(np.float32)               # IEEE fp32 division
+    zero = s == 0
+    safe = np.where(zero, np.float32(1.0), s)
+    y = (xf / safe[:, None]).astype(np.float32)        # IEEE fp32 division
+    y = np.clip(y, -F448, F448)
+    q = e4m3.encode(y)
+    q[zero] = 0                                         # all-zero group
+    return q, s
+
+
+def act_quant_block(x_bits: np.ndarray, block: int = 128):
+    """1x128 block quantization of a bf16 [M, K] tensor.
+
+    Returns ``(q, s)``: ``q`` uint8 e4m3 codes [M, K] and ``s`` float32 scales
+    [M, K // block] (block b of row m covers columns b*block .. b*block+block-1).
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    M, K = x_bits.shape
+    if K % block:
+        raise ValueError("K must be a multiple of the block size")
+    xf = bf16_to_f32(x_bits).reshape(M * (K // block), block)
+    q, s = _quant_groups(xf)
+    return q.reshape(M, K), s.reshape(M, K // block)
+
+
+def amax_tensor(x_bits: np.ndarray) -> np.float32:
+    """Exact amax of a bf16 tensor, as float32."""
+    return np.max(np.abs(bf16_to_f32(x_bits)))
+
+
+def amax_quant_tensor(x_bits: np.ndarray):
+    """Per-tensor dynamic quantization of a bf16 tensor of any shape.
+
+    Returns ``(q, s)``: uint8 codes of the same shape and a float32 scalar.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    xf = bf16_to_f32(x_bits).reshape(1, -1)
+    q, s = _quant_groups(xf)
+    return q.reshape(x_bits.shape), np.float32(s[0])
+
+
+def weight_quant_block(w_bits: np.ndarray, block: int = 128):
+    """128x128 block quantization of a bf16 [N, K] weight.
+
+    Returns ``(q, s)``: uint8 codes [N, K] and float32 scales
+    [N // block, K // block].
+    """
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    N, K = w_bits.shape
+    if N % block or K % block:
+        raise ValueError("N and K must be multiples of the block size")
+    nb, kb = N // block, K // block
+    wf = bf16_to_f32(w_bits).reshape(nb, block, kb, block).transpose(0, 2, 1, 3)
+    q, s = _quant_groups(wf.reshape(nb * kb, block * block))
+    q = q.reshape(nb, kb, block, block).transpose(0, 2, 1, 3).reshape(N, K)
+    return np.ascontiguousarray(q), s.reshape(nb, kb)

@@ -1,0 +1,143 @@
+"""Pins for the oracle's block-scaled GEMM and its comparison rule (CPU only).
+
+Independent checks:
+* unit scales: the float64 reference equals an int64 brute force exactly
+  (every e4m3 value is an integer multiple of 2**-9, so products are integer
+  multiples of 2**-18 and the sums are exact);
+* exact rational brute force in the pages' block form
+  sum_b sa[m,b] * sw[n//128,b] * sum_{k in b} A[m,k] W[n,k], with random fp32
+  block scales, on shapes with several row and column blocks (M != N != K so
+  that a transposed operand or scale fails);
+* identity weight: W = I (N = K) and sw = 1 give R = dequantized A;
+* the comparison accepts the correctly rounded reference and rejects a result
+  with one block scale missing.
+"""
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+from oracle import e4m3, gemm
+
+FINITE = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+
+
+def rand_codes(rng, shape):
+    return rng.choice(FINITE, size=shape).astype(np.uint8)
+
+
+def test_unit_scales_equal_int64_bruteforce():
+    rng = np.random.default_rng(1)
+    M, N, K = 5, 256, 384
+    qa, qw = rand_codes(rng, (M, K)), rand_codes(rng, (N, K))
+    sa = np.ones((M, K // 128), np.float32)
+    sw = np.ones((N // 128, K // 128), np.float32)
+    R = gemm.gemm_blockscaled_ref(qa, sa, qw, sw)
+    ia = (e4m3.DECODE[qa] * 2 ** 9).astype(np.int64)
+    iw = (e4m3.DECODE[qw] * 2 ** 9).astype(np.int64)
+    exact = ia @ iw.T
+    assert np.array_equal(R * 2.0 ** 18, exact.astype(np.float64))
+
+
+def test_fraction_bruteforce_block_form():
+    rng = np.random.default_rng(2)
+    M, N, K = 3, 256, 384
+    qa, qw = rand_codes(rng, (M, K)), rand_codes(rng, (N, K))
+    sa = (10.0 ** rng.uniform(-3, 1, size=(M, K // 128))).astype(np.float32)
+    sw = (10.0 ** rng.uniform(-4, -1, size=(N // 128, K // 128))).astype(np.float32)
+    R = gemm.gemm_blockscaled_ref(qa, sa, qw, sw)
+    S = gemm.gemm_abs_ref(qa, sa, qw, sw)
+    dec = [Fraction(float(v)) if np.isfinite(v) else None for v in e4m3.DECODE]
+    cols = [0, 1, 127, 128, 200, 255]
+    for m in range(M):
+        for n in cols:
+            tot, atot = Fraction(0), Fraction(0)
+            for b in range(K // 128):
+                part, apart = Fraction(0), Fraction(0)
+                for k in range(b * 128, (b + 1) * 128):
+                    p = dec[qa[m, k]] * dec[qw[n, k]]
+                    part += p
+                    apart += abs(p)
+                scale = Fraction(float(sa[m, b])) * Fraction(float(sw[n // 128, b]))
+                tot += scale * part
+                atot += scale * apart
+            # float64 reference within one rounding per product sum of |terms|
+            assert abs(Fraction(float(R[m, n])) - tot) <= atot * Fraction(K + 2, 2 ** 53)
+            assert abs(Fraction(float(S[m, n])) - atot) <= atot * Fraction(K + 2, 2 ** 53)
+
+
+def test_identity_weight():
+    rng = np.random.default_rng(3)
+    M, K = 7, 256
+    qa = rand_codes(rng, (M, K))
+    sa = (10.0 ** rng.uniform(-2, 2, size=(M, K // 128))).astype(np.float32)
+    qw = np.zeros((K, K), np.uint8)
+    np.fill_diagonal(qw, 0x38)                      # 1.0
+    sw = np.ones((K // 128, K // 128), np.float32)
+    R = gemm.gemm_blockscaled_ref(qa, sa, qw, sw)
+    Abar = e4m3.DECODE[qa] * np.repeat(sa.astype(np.float64), 128, axis=1)
+    assert np.array_equal(R, Abar)
+
+
+def test_scale_indexing_is_per_block():
+    # one activation block scale and one weight block scale doubled: only the
+    # matching (row, K block) and (column block, K block) terms change
+    rng = np.random.default_rng(4)
+    M, N, K = 4, 384, 256
+    qa, qw = rand_codes(rng, (M, K)), rand_codes(rng, (N, K))
+    sa = np.ones((M, K // 128), np.float32)
+    sw = np.ones((N // 128, K // 128), np.float32)
+    base = gemm.gemm_blockscaled_ref(qa, sa, qw, sw)
+    sa2 = sa.copy(); sa2[2, 1] = 2.0
+    d = gemm.gemm_blockscaled_ref(qa, sa2, qw, sw) - base
+    blk = (e4m3.DECODE[qa[2, 128:]] @ e4m3.DECODE[qw[:, 128:]].T)
+    assert np.array_equal(d[2], blk) and not d[[0, 1, 3]].any()
+    sw2 = sw.copy(); sw2[1, 0] = 4.0
+    d = gemm.gemm_blockscaled_ref(qa, sa, qw, sw2) - base
+    blk = 3.0 * (e4m3.DECODE[qa[:, :128]] @ e4m3.DECODE[qw[128:256, :128]].T)
+    assert np.array_equal(d[:, 128:256], blk)
+    assert not d[:, :128].any() and not d[:, 256:].any()
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal(200_000).astype(np.float32) * np.float32(1000.0)
+    v = np.concatenate([v, np.float32([0.0, -0.0, 1.00390625, 1.01171875, 3e38, 1e-40])])
+    ours = gemm.f64_to_bf16_rne(v.astype(np.float64))
+    theirs = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, theirs)
+
+
+def test_compare_accepts_reference_and_rejects_missing_scale():
+    rng = np.random.default_rng(6)
+    M, N, K = 8, 256, 512
+    qa, qw = rand_codes(rng, (M, K)), rand_codes(rng, (N, K))
+    sa = (10.0 ** rng.uniform(-2, 0, size=(M, K // 128))).astype(np.float32)
+    sw = (10.0 ** rng.uniform(-3, -1, size=(N // 128, K // 128))).astype(np.float32)
+    R = gemm.gemm_blockscaled_ref(qa, sa, qw, sw)
+    S = gemm.gemm_abs_ref(qa, sa, qw, sw)
+    good = gemm.f64_to_bf16_rne(R)
+    res = gemm.compare_gemm(good, R, S, K)
+    assert res["ok"], res
+    sa_bad = sa.copy(); sa_bad[:, 2] = 1.0
+    bad = gemm.f64_to_bf16_rne(gemm.gemm_blockscaled_ref(qa, sa_bad, qw, sw))
+    res = gemm.compare_gemm(bad, R, S, K)
+    assert not res["ok"], res
+    # transposed weight blocks are rejected too
+    bad = gemm.f64_to_bf16_rne(gemm.gemm_blockscaled_ref(qa, sa, qw, sw[::-1]))
+    assert not gemm.compare_gemm(bad, R, S, K)["ok"]
+
+
+def test_rows_sampler_matches_full():
+    rng = np.random.default_rng(7)
+    M, N, K = 6, 256, 256
+    qa, qw = rand_codes(rng, (M, K)), rand_codes(rng, (N, K))
+    sa = rng.uniform(0.1, 2, size=(M, K // 128)).astype(np.float32)
+    sw = rng.uniform(0.1, 2, size=(N // 128, K // 128)).astype(np.float32)
+    R = gemm.gemm_blockscaled_ref(qa, sa, qw, sw)
+    S = gemm.gemm_abs_ref(qa, sa, qw, sw)
+    rows = np.array([0, 5, 3, 3]); cols = np.array([255, 0, 128, 127])
+    r, s = gemm.gemm_rows_ref(qa, sa, qw, sw, rows, cols)
+    # same sums in another order: equal up to fp64 summation error
+    assert np.all(np.abs(r - R[rows, cols]) <= K * 2.0 ** -52 * S[rows, cols])
+    assert np.all(np.abs(s - S[rows, cols]) <= K * 2.0 ** -52 * S[rows, cols])

@@ -1,0 +1,254 @@
+"""Pins for the oracle's block, per-tensor and weight quantizers (CPU only).
+
+Independent checks:
+* exact rational brute force (fractions.Fraction): the scale is the binary32
+  value nearest to amax/448 and each code is the e4m3 value nearest to the
+  binary32 value nearest to x/s, found by search over all codes;
+* an exhaustive grid over every (bf16 significand of the block maximum,
+  bf16 significand of an element) pair, checked against a float64-division
+  computation (a double-precision quotient of two binary32 values rounded once
+  to binary32 is the correctly rounded binary32 quotient, since 53 >= 2*24+2),
+  and shown to catch the plausible mistake of multiplying by a reciprocal;
+* invariants: amax is the largest |x|, the element(s) at amax encode to +-448,
+  every code is within half an e4m3 step of the clamped quotient, zero blocks
+  give scale 0 and zero codes;
+* known answers: blocks of e4m3 values times 2**j with maximum 448 * 2**j have
+  scale exactly 2**j and reproduce their own codes.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import e4m3, quant
+
+F448 = np.float32(448.0)
+
+
+# --------------------------------------------------------------------------
+# exact helpers written for the tests (no oracle code)
+
+def fl32(r: Fraction) -> Fraction:
+    """Round a rational to binary32, nearest with ties to even (no overflow)."""
+    if r == 0:
+        return Fraction(0)
+    neg = r < 0
+    r = -r if neg else r
+    e = r.numerator.bit_length() - r.denominator.bit_length()
+    while Fraction(2) ** e > r:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= r:
+        e += 1
+    e = max(e, -126)
+    quantum = Fraction(2) ** (e - 23)
+    n = r / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    out = fl * quantum
+    return -out if neg else out
+
+
+POS_CODES = [(c, Fraction(float(e4m3.DECODE[c]))) for c in range(0x7F)]
+
+
+def nearest_e4m3(y: Fraction, negative: bool) -> int:
+    a = min(abs(y), Fraction(448))
+    best = None
+    for c, v in POS_CODES:
+        d = abs(v - a)
+        if best is None or d < best[1] or (d == best[1] and c % 2 == 0):
+            best = (c, d)
+    return best[0] | (0x80 if negative else 0)
+
+
+def bf16_value(bits) -> Fraction:
+    return Fraction(float(quant.bf16_to_f32(np.array([bits], np.uint16))[0]))
+
+
+def brute_group(bits_list):
+    """Scale and codes of one group by exact arithmetic."""
+    vals = [bf16_value(b) for b in bits_list]
+    amax = max(abs(v) for v in vals)
+    s = fl32(amax / 448)
+    if s == 0:
+        return 0.0, [0] * len(vals)
+    codes = []
+    for b, v in zip(bits_list, vals):
+        y = fl32(v / s)
+        codes.append(nearest_e4m3(y, negative=bool(int(b) & 0x8000)))
+    return float(s), codes
+
+
+def nearest_code_vec(v32):
+    """Vectorised nearest search (same rule as nearest_e4m3)."""
+    pos = e4m3.DECODE[:0x7F]
+    a = np.minimum(np.abs(v32.astype(np.float64)), 448.0)
+    i = np.searchsorted(pos, a, side="left")
+    hi = np.clip(i, 0, 0x7E)
+    lo = np.clip(i - 1, 0, 0x7E)
+    dlo, dhi = a - pos[lo], pos[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & ((hi & 1) == 0))
+    return np.where(pick_hi, hi, lo).astype(np.uint8) | (np.signbit(v32).astype(np.uint8) << 7)
+
+
+def widen(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------
+
+def test_block_quant_fraction_bruteforce():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((3, 256)) * np.array([[1.0], [1e-3], [50.0]])
+    x[1, 5] = 7e3                      # one outlier block
+    x[2, 128:] = 0.0                   # one zero block
+    bits = synth.f64_to_bf16_bits(x)
+    q, s = quant.act_quant_block(bits)
+    assert q.shape == (3, 256) and s.shape == (3, 2) and s.dtype == np.float32
+    for m in range(3):
+        for b in range(2):
+            es, ec = brute_group(list(bits[m, b * 128:(b + 1) * 128]))
+            assert float(s[m, b]) == es, (m, b)
+            assert list(q[m, b * 128:(b + 1) * 128]) == ec, (m, b)
+
+
+def test_special_blocks_fraction_bruteforce():
+    blocks = synth.special_blocks()
+    q, s = quant.act_quant_block(blocks)
+    for i in range(blocks.shape[0]):
+        es, ec = brute_group(list(blocks[i]))
+        assert float(s[i, 0]) == es, i
+        assert list(q[i]) == ec, i
+
+
+def test_quotient_grid_exhaustive():
+    g = synth.quotient_grid()
+    q, s = quant.act_quant_block(g)
+    xf = widen(g)
+    amax = np.max(np.abs(xf), axis=1)
+    s_ref = (amax.astype(np.float64) / 448.0).astype(np.float32)
+    assert np.array_equal(s[:, 0].view(np.uint32), s_ref.view(np.uint32))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = (xf.astype(np.float64) / s_ref.astype(np.float64)[:, None]).astype(np.float32)
+    q_ref = nearest_code_vec(y)
+    q_ref[s_ref == 0] = 0
+    assert np.array_equal(q, q_ref)
+    # the grid is sharp enough to reject a reciprocal multiply in place of x/s
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        r = (np.float32(1.0) / s_ref).astype(np.float32)
+        y_bad = (xf * r[:, None]).astype(np.float32)
+    q_bad = nearest_code_vec(y_bad)
+    assert np.count_nonzero(q_bad != q_ref) > 0
+
+
+def test_amax_invariants():
+    rng = np.random.default_rng(3)
+    bits = synth.f64_to_bf16_bits(rng.standard_t(3.0, size=(5, 384)))
+    vals = [float(v) for v in widen(bits).reshape(-1)]
+    amax = quant.amax_tensor(bits)
+    assert float(amax) == max(abs(v) for v in vals)
+    perm = rng.permutation(bits.size)
+    assert quant.amax_tensor(bits.reshape(-1)[perm]) == amax
+    # per block: the scale times 448 brackets the block maximum
+    _, s = quant.act_quant_block(bits)
+    for m in range(5):
+        for b in range(3):
+            blk = vals[m * 384 + b * 128: m * 384 + (b + 1) * 128]
+            bm = max(abs(v) for v in blk)
+            assert float(s[m, b]) == float(fl32(Fraction(bm) / 448))
+
+
+def test_max_element_encodes_to_448_and_half_step():
+    bits = synth.gen_c1()["a"]
+    q, s = quant.act_quant_block(bits)
+    xf = widen(bits).reshape(-1, 128)
+    qb = q.reshape(-1, 128)
+    sb = s.reshape(-1)
+    zero = sb == 0
+    assert np.all(qb[zero] == 0) and zero.sum() == 1
+    amax = np.max(np.abs(xf), axis=1)
+    at_max = (np.abs(xf) == amax[:, None]) & ~zero[:, None]
+    assert np.all((qb[at_max] & 0x7F) == 0x7E)
+    # every code within half an e4m3 step of the clamped binary32 quotient
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = np.clip((xf / sb[:, None]).astype(np.float32), -F448, F448)[~zero].astype(np.float64)
+    d = e4m3.decode(qb[~zero])
+    a = np.abs(y)
+    gap = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
+    assert np.all(np.abs(d - y) <= gap / 2)
+
+
+def test_known_answer_power_of_two_scales():
+    rng = np.random.default_rng(5)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    rows, want_q, want_s = [], [], []
+    for j in range(-8, 8):
+        codes = rng.choice(finite, size=128)
+        codes[rng.integers(0, 128)] = 0x7E if j % 2 else 0xFE
+        codes[np.abs(e4m3.DECODE[codes]) == 448] = 0x7E if j % 2 else 0xFE
+        vals = e4m3.DECODE[codes] * 2.0 ** j
+        rows.append(synth.f64_to_bf16_bits(vals))
+        want_q.append(codes)
+        want_s.append(2.0 ** j)
+    bits = np.stack(rows).reshape(-1, 256)             # two blocks per row
+    q, s = quant.act_quant_block(bits)
+    assert np.array_equal(q.reshape(-1, 128), np.stack(want_q).astype(np.uint8))
+    assert np.array_equal(s.reshape(-1), np.array(want_s, np.float32))
+
+
+def test_block_axis_and_shape():
+    # rows of very different magnitude: blocks run along K within one row
+    M, K = 4, 512
+    x = np.ones((M, K)) * np.array([[1.0], [2.0], [4.0], [8.0]])
+    x[:, 128:256] *= 1000.0
+    q, s = quant.act_quant_block(synth.f64_to_bf16_bits(x))
+    for m in range(M):
+        for b in range(K // 128):
+            assert s[m, b] == np.float32(x[m, b * 128] / 448.0)
+    assert np.all((q & 0x7F) == 0x7E)
+    with pytest.raises(ValueError):
+        quant.act_quant_block(np.zeros((2, 100), np.uint16))
+
+
+def test_per_tensor_rules():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((3, 128))
+    x[2, 17] = -300.0                                  # the tensor maximum
+    bits = synth.f64_to_bf16_bits(x)
+    q, s = quant.amax_quant_tensor(bits)
+    es, ec = brute_group(list(bits.reshape(-1)))
+    assert float(s) == es
+    assert list(q.reshape(-1)) == ec
+    assert q.shape == bits.shape
+    # one 1x128 block: per-tensor and block quantization agree
+    q1, s1 = quant.amax_quant_tensor(bits[:1])
+    qb, sb = quant.act_quant_block(bits[:1])
+    assert np.array_equal(q1, qb) and s1 == sb[0, 0]
+    # all zeros
+    qz, sz = quant.amax_quant_tensor(np.full((2, 64), 0x8000, np.uint16))
+    assert sz == 0 and np.all(qz == 0)
+
+
+def test_weight_quant_block_rules():
+    rng = np.random.default_rng(13)
+    N, K = 256, 384                                    # N != K: catches transposed blocks
+    w = rng.standard_normal((N, K)) * 0.02
+    mult = 2.0 ** rng.integers(-6, 7, size=(N // 128, K // 128))
+    w *= np.repeat(np.repeat(mult, 128, axis=0), 128, axis=1)
+    bits = synth.f64_to_bf16_bits(w)
+    q, s = quant.weight_quant_block(bits)
+    assert q.shape == (N, K) and s.shape == (N // 128, K // 128)
+    for i in range(N // 128):
+        for j in range(K // 128):
+            blk = bits[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
+            qq, ss = quant.amax_quant_tensor(blk)
+            assert s[i, j] == ss
+            assert np.array_equal(q[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128], qq)
+    # spot-check one block against exact arithmetic
+    blk = bits[128:256, 256:384].reshape(-1)
+    es, ec = brute_group(list(blk[:1]) + list(blk))   # same max set
+    amax = max(abs(bf16_value(b)) for b in blk)
+    assert float(s[1, 2]) == float(fl32(amax / 448))
