@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 quantize-and-multiply path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5|c4|c3|c2|c1] [--M m]
+                    [--graph] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one batch of synthetic input, with
+the inputs resident in HBM before timing starts. Default workload (c5, the
+large-M stress case M=16384, N=7168, K=2048): 1x128 block act-quant of A,
+per-tensor amax quant of A, block-scaled FP8 GEMM with bf16 output. Other
+workloads: c4 prefill (act-quant + GEMM, 4096x4096x7168), c3 decode (M tokens,
+N=2048, K=7168), c2 per-tensor sweep (K=2048), c1 tiny (32x512x512).
+
+Prints ONE JSON line. ``value`` is the step throughput expressed as GEMM
+TFLOP/s (2*M*N*K per step / step time; per-tensor-only workloads use GB/s).
+The per-stage times come from HIP events recorded around each launch inside
+the timed region on the launch stream; ``roofline`` is for the dominant
+kernel. ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 MFMA, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="c5", choices=["c5", "c4", "c3", "c2", "c1"])
+    p.add_argument("--M", type=int, default=None, help="rows for c2/c3")
+    p.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
+    p.add_argument("--rotate", type=int, default=3, help="input copies rotated across steps")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=None, help="rows of the CPU oracle sample")
+    return p.parse_args()
+
+
+def src_hash(name):
+    with open(os.path.join(ROOT, "fp8_block_scaled_act_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_key, src):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    the kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = d.get(kernel_key)
+    if not e or e.get("src_sha256_16") != src_hash(src):
+        return None
+    return e.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# workloads: synthetic inputs -> device tensors, and the per-stage launches
+
+class Workload:
+    def __init__(self, args, torch, fb):
+        import synth
+        self.torch, self.fb = torch, fb
+        dev = "cuda:0"
+        w = args.workload
+        self.name = w
+        self.stages = []          # (name, fn(i) -> None, algorithmic bytes, flops)
+        rot = max(1, args.rotate)
+
+        def bf16(bits):
+            t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+            return t.to(dev)
+
+        if w == "c2":
+            M = args.M or 65536
+            K = 2048
+            x = bf16(synth.gen_c2(M)["x"])
+            xs = [x] + [x.clone() for _ in range(rot - 1)]
+            numel = M * K
+            q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+            s = torch.empty((1,), dtype=torch.float32, device=dev)
+            wsb = fb.fp8_amax_quant_tensor_workspace_bytes(numel)
+            ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device=dev)
+            self.stages.append(("amax_quant_tensor",
+                                lambda i: fb.fp8_amax_quant_tensor(xs[i % rot], out=(q, s), workspace=ws),
+                                3 * numel + 4, 0))
+            self.config = {"workload": f"per-tensor dynamic quant, X bf16 [{M}, {K}]", "M": M, "K": K}
+            self.M, self.N, self.K = M, 0, K
+            self.cpu = ("c2", M, K, None)
+            return
+
+        if w == "c1":
+            d = synth.gen_c1(); M, N, K = 32, 512, 512
+            wl = "tiny block quant + GEMM, A [32,512], W [512,512]"
+        elif w == "c3":
+            M = args.M or 64
+            d = synth.gen_c3(M); N, K = 2048, 7168
+            wl = f"decode block-scaled GEMM, M={M}, N=2048, K=7168"
+        elif w == "c4":
+            d = synth.gen_c4(); M, N, K = 4096, 4096, 7168
+            wl = "prefill block-scaled GEMM, M=4096, N=4096, K=7168"
+        else:
+            d = synth.gen_c5(); M, N, K = 16384, 7168, 2048
+            wl = "large-M stress: block act-quant + per-tensor quant + block-scaled GEMM, M=16384, N=7168, K=2048"
+        self.M, self.N, self.K = M, N, K
+        a = bf16(d["a"])
+        wq, wsc = fb.fp8_weight_quant_block(bf16(d["w"]))
+        if "w_scale" in d:
+            wsc = torch.from_numpy(d["w_scale"]).to(dev)
+        a_s = [a] + [a.clone() for _ in range(rot - 1)]
+        w_s = [wq] + [wq.clone() for _ in range(rot - 1)]
+        qa = [torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev) for _ in range(rot)]
+        sa = [torch.empty((M, K // 128), dtype=torch.float32, device=dev) for _ in range(rot)]
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        gwsb = fb.fp8_gemm_blockscaled_workspace_bytes(M, N, K)
+        gws = torch.empty((max(gwsb, 16),), dtype=torch.uint8, device=dev)
+        self.stages.append(("act_quant_block",
+                            lambda i: fb.fp8_act_quant_block(a_s[i % rot], out=(qa[i % rot], sa[i % rot])),
+                            2 * M * K + M * K + 4 * (M * K // 128), 0))
+        if w == "c5":
+            qt = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+            st = torch.empty((1,), dtype=torch.float32, device=dev)
+            twsb = fb.fp8_amax_quant_tensor_workspace_bytes(M * K)
+            tws = torch.empty((max(twsb, 16),), dtype=torch.uint8, device=dev)
+            self.stages.append(("amax_quant_tensor",
+                                lambda i: fb.fp8_amax_quant_tensor(a_s[i % rot], out=(qt, st), workspace=tws),
+                                3 * M * K + 4, 0))
+        gemm_bytes = M * K + 4 * M * (K // 128) + N * K + 4 * (N // 128) * (K // 128) + 2 * M * N
+        self.stages.append(("gemm_blockscaled",
+                            lambda i: fb.fp8_gemm_blockscaled(qa[i % rot], sa[i % rot], w_s[i % rot], wsc,
+                                                              out=c, workspace=gws),
+                            gemm_bytes, 2 * M * N * K))
+        self.config = {"workload": wl, "M": M, "N": N, "K": K}
+        self.cpu = (w, M, K, N)
+
+
+def time_steps(torch, wl, steps, warmup, graph):
+    """Warm up, then time exactly `steps` steps; per-stage HIP events on the
+    launch stream (torch's current stream, where the library enqueues)."""
+    st = torch.cuda.current_stream()
+    nst = len(wl.stages)
+    for i in range(warmup):
+        for _, fn, _, _ in wl.stages:
+            fn(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(st)
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(steps):
+                    for _, fn, _, _ in wl.stages:
+                        fn(i)
+        torch.cuda.synchronize()
+        g.replay()                                       # one untimed replay
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st); g.replay(); e1.record(st)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        total_ms = e0.elapsed_time(e1)
+        return total_ms / steps, None, wall
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True); end = torch.cuda.Event(enable_timing=True)
+    start.record(st)
+    for i in range(steps):
+        ev[i][0].record(st)
+        for j, (_, fn, _, _) in enumerate(wl.stages):
+            fn(warmup + i)
+            ev[i][j + 1].record(st)
+    end.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_stage = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(nst)] for i in range(steps)])
+    return start.elapsed_time(end) / steps, per_stage, wall
+
+
+def cpu_baseline(wl, rows_arg):
+    """The oracle, as it stands, on a bounded row sample of the same workload."""
+    import synth
+    from oracle import gemm as ogemm, quant as oquant
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = os.cpu_count() or 1
+    kind, M, K, N = wl.cpu
+    t = 0.0
+    if kind == "c2":
+        rows = min(M, rows_arg or 4096)
+        x = synth.gen_c2(rows)["x"]
+        t0 = time.perf_counter(); oquant.amax_quant_tensor(x); t = time.perf_counter() - t0
+        value = (3 * rows * K + 4) / t / 1e9
+        return {"value": value, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"per-tensor quant of [{rows}, {K}] bf16 (numpy, one thread), {t:.2f} s"}
+    rows = min(M, rows_arg or {"c5": 2048, "c4": 1024, "c3": M, "c1": M}[kind])
+    d = {"c1": lambda: synth.gen_c1(), "c3": lambda: synth.gen_c3(M), "c4": lambda: synth.gen_c4(),
+         "c5": lambda: synth.gen_c5()}[kind]()
+    a = d["a"][:rows]
+    qw, sw = oquant.weight_quant_block(d["w"])          # offline step, not timed
+    if "w_scale" in d:
+        sw = d["w_scale"]
+    t0 = time.perf_counter()
+    qa, sa = oquant.act_quant_block(a)
+    if kind == "c5":
+        oquant.amax_quant_tensor(a)
+    ogemm.gemm_blockscaled_ref(qa, sa, qw, sw)
+    t = time.perf_counter() - t0
+    value = 2.0 * rows * N * K / t / 1e12
+    return {"value": value, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": (f"rows 0..{rows - 1} of A ({rows} of {M}): block quant"
+                       + (" + per-tensor quant" if kind == "c5" else "")
+                       + f" (numpy, one thread) + fp64 GEMM {rows}x{N}x{K} (BLAS, {blas_threads} threads); "
+                       f"{t:.2f} s; value = 2*rows*N*K / time")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    import fp8_block_scaled_act_amd as fb
+    fb.lib()
+    torch.cuda.set_device(0)
+    wl = Workload(args, torch, fb)
+    ms, per_stage, wall = time_steps(torch, wl, args.steps, args.warmup, args.graph)
+
+    stages = {}
+    dominant = None
+    for j, (name, _, nbytes, flops) in enumerate(wl.stages):
+        e = {"algorithmic_bytes": nbytes}
+        if per_stage is not None:
+            us = float(np.mean(per_stage[:, j])) * 1e3
+            e["us_mean"] = us
+            e["us_p10"] = float(np.percentile(per_stage[:, j], 10)) * 1e3
+            e["us_p90"] = float(np.percentile(per_stage[:, j], 90)) * 1e3
+            e["GB/s"] = nbytes / (us * 1e-6) / 1e9
+            e["hbm_frac"] = e["GB/s"] / HBM_PEAK_GBS
+            if flops:
+                e["TFLOP/s"] = flops / (us * 1e-6) / 1e12
+                e["mfma_frac"] = e["TFLOP/s"] / FP8_PEAK_TFLOPS
+        stages[name] = e
+    # dominant kernel: the GEMM when present (prefill: MFMA-bound; decode: HBM-bound)
+    if "gemm_blockscaled" in stages:
+        dominant = "gemm_blockscaled"
+    else:
+        dominant = wl.stages[0][0]
+    roofline = None
+    ds = stages[dominant]
+    if per_stage is not None:
+        src = "gemm.hip" if dominant == "gemm_blockscaled" else "quant.hip"
+        traffic = load_traffic(f"{dominant}:{args.workload}", src)
+        if dominant == "gemm_blockscaled" and 2 * wl.M * wl.N * wl.K / max(ds["algorithmic_bytes"], 1) > 625:
+            roofline = {"bound": "mfma", "achieved": ds["TFLOP/s"], "peak": FP8_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": ds["TFLOP/s"] / FP8_PEAK_TFLOPS, "traffic": traffic}
+        else:
+            roofline = {"bound": "hbm", "achieved": ds["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": ds["GB/s"] / HBM_PEAK_GBS, "traffic": traffic}
+        roofline["kernel"] = dominant
+        roofline["us_per_launch"] = ds["us_mean"]
+
+    if wl.N:
+        value = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
+        unit = "TFLOP/s"
+    else:
+        value = wl.stages[0][2] / (ms * 1e-3) / 1e9
+        unit = "GB/s"
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_rows)
+        cpu["host_cpus"] = os.cpu_count()
+        try:
+            cpu["affinity_cpus"] = len(os.sched_getaffinity(0))
+        except AttributeError:  # pragma: no cover
+            pass
+
+    line = {
+        "metric": "FP8 block-scaled GEMM TFLOP/s + act-quant GB/s (%roofline), 1 MI355X",
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 in/out)",
+        "data": "synthetic (seeded numpy generators; inputs resident in HBM, "
+                f"{max(1, args.rotate)} rotated copies)",
+        "config": wl.config,
+        "timing": "HIP graph replay" if args.graph else "HIP events per stage on the launch stream",
+        "stages": stages,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "wall_s_timed_region": wall,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

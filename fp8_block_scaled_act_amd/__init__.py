@@ -1,0 +1,224 @@
+"""Python binding of libfp8bs (FP8 e4m3 quantize-and-multiply path for MI355X).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libfp8bs.so`` (C ABI in ``include/fp8bs.h``). PyTorch provides device memory
+and the current stream. There is no CPU fallback: if the library is missing
+or cannot be loaded, every call raises.
+
+Entry points (same names as the C ABI):
+    fp8_act_quant_block(x)           -> (q, s)   x bf16 [M, K]; s fp32 [M, K/128]
+    fp8_amax_quant_tensor(x)         -> (q, s)   any shape; s fp32 [1]
+    fp8_gemm_blockscaled(a, sa, w, sw) -> c      c bf16 [M, N] = A . W^T
+    fp8_weight_quant_block(w)        -> (q, s)   w bf16 [N, K]; s fp32 [N/128, K/128]
+``q`` tensors are ``torch.float8_e4m3fn`` (the OCP e4m3 "fn" bytes). Each
+function also accepts preallocated outputs (``out=``) so that a caller can
+time or graph-capture calls without allocations.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LIB_PATH",
+    "lib",
+    "Fp8bsError",
+    "fp8_act_quant_block",
+    "fp8_amax_quant_tensor",
+    "fp8_amax_quant_tensor_workspace_bytes",
+    "fp8_gemm_blockscaled",
+    "fp8_gemm_blockscaled_workspace_bytes",
+    "fp8_weight_quant_block",
+    "debug_encode_e4m3",
+    "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8bs.so")
+
+EXPORTED_SYMBOLS = (
+    "fp8bs_status_string",
+    "fp8_act_quant_block",
+    "fp8_amax_quant_tensor_workspace_bytes",
+    "fp8_amax_quant_tensor",
+    "fp8_gemm_blockscaled_workspace_bytes",
+    "fp8_gemm_blockscaled",
+    "fp8_weight_quant_block",
+    "fp8bs_debug_encode_e4m3",
+)
+
+E4M3 = torch.float8_e4m3fn
+
+
+class Fp8bsError(RuntimeError):
+    """A non-zero status from libfp8bs."""
+
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: {text} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfp8bs.so (once). Raises if it is missing: no fallback path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m fp8_block_scaled_act_amd.build`"
+        )
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, sz, fp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    L.fp8bs_status_string.argtypes = [ctypes.c_int]
+    L.fp8bs_status_string.restype = ctypes.c_char_p
+    L.fp8_act_quant_block.argtypes = [vp, i64, i64, vp, fp, vp]
+    L.fp8_act_quant_block.restype = ctypes.c_int
+    L.fp8_amax_quant_tensor_workspace_bytes.argtypes = [i64]
+    L.fp8_amax_quant_tensor_workspace_bytes.restype = sz
+    L.fp8_amax_quant_tensor.argtypes = [vp, i64, vp, fp, vp, sz, vp]
+    L.fp8_amax_quant_tensor.restype = ctypes.c_int
+    L.fp8_gemm_blockscaled_workspace_bytes.argtypes = [i64, i64, i64]
+    L.fp8_gemm_blockscaled_workspace_bytes.restype = sz
+    L.fp8_gemm_blockscaled.argtypes = [vp, fp, vp, fp, vp, i64, i64, i64, vp, sz, vp]
+    L.fp8_gemm_blockscaled.restype = ctypes.c_int
+    L.fp8_weight_quant_block.argtypes = [vp, i64, i64, vp, fp, vp]
+    L.fp8_weight_quant_block.restype = ctypes.c_int
+    L.fp8bs_debug_encode_e4m3.argtypes = [fp, vp, i64, vp]
+    L.fp8bs_debug_encode_e4m3.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise Fp8bsError(fn, rc, lib().fp8bs_status_string(rc).decode())
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (strided views are not supported)")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def fp8_act_quant_block(x: torch.Tensor, out=None):
+    """1x128 block quantization of bf16 ``x`` [M, K] (K % 128 == 0)."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    if out is None:
+        q = torch.empty((M, K), dtype=E4M3, device=x.device)
+        s = torch.empty((M, K // 128 if K % 128 == 0 else 1), dtype=torch.float32, device=x.device)
+    else:
+        q, s = out
+    with torch.cuda.device(x.device):
+        rc = lib().fp8_act_quant_block(_ptr(x), M, K, _ptr(q), _ptr(s), ctypes.c_void_p(_stream(x.device)))
+    _check("fp8_act_quant_block", rc)
+    return q, s
+
+
+def fp8_amax_quant_tensor_workspace_bytes(numel: int) -> int:
+    return int(lib().fp8_amax_quant_tensor_workspace_bytes(int(numel)))
+
+
+def fp8_amax_quant_tensor(x: torch.Tensor, out=None, workspace=None):
+    """Per-tensor quantization of bf16 ``x`` (any shape) with an exact amax."""
+    _need(x, "x", torch.bfloat16)
+    numel = x.numel()
+    if out is None:
+        q = torch.empty(x.shape, dtype=E4M3, device=x.device)
+        s = torch.empty((1,), dtype=torch.float32, device=x.device)
+    else:
+        q, s = out
+    wsb = fp8_amax_quant_tensor_workspace_bytes(numel) if numel > 0 else 0
+    if workspace is None and wsb > 0:
+        workspace = torch.empty((wsb,), dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        rc = lib().fp8_amax_quant_tensor(
+            _ptr(x), numel, _ptr(q), _ptr(s), _ptr(workspace),
+            workspace.numel() if workspace is not None else 0, ctypes.c_void_p(_stream(x.device)))
+    _check("fp8_amax_quant_tensor", rc)
+    return q, s
+
+
+def fp8_gemm_blockscaled_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().fp8_gemm_blockscaled_workspace_bytes(int(M), int(N), int(K)))
+
+
+def _as_u8(t):
+    return t.view(torch.uint8) if t.dtype == E4M3 else t
+
+
+def fp8_gemm_blockscaled(a, a_scale, w, w_scale, out=None, workspace=None):
+    """C = A . W^T (bf16 [M, N]) from e4m3 A [M, K] with 1x128 scales and e4m3
+    W [N, K] with 128x128 scales."""
+    for t, n in ((a, "a"), (w, "w")):
+        if t.dtype not in (E4M3, torch.uint8):
+            raise TypeError(f"{n} must be float8_e4m3fn (or its uint8 bytes)")
+    a, w = _as_u8(a), _as_u8(w)
+    _need(a, "a", torch.uint8)
+    _need(w, "w", torch.uint8, a.device)
+    _need(a_scale, "a_scale", torch.float32, a.device)
+    _need(w_scale, "w_scale", torch.float32, a.device)
+    if a.dim() != 2 or w.dim() != 2 or a.shape[1] != w.shape[1]:
+        raise ValueError("a must be [M, K] and w [N, K]")
+    M, K = a.shape
+    N = w.shape[0]
+    if a_scale.shape != (M, K // 128) or w_scale.shape != (N // 128, K // 128):
+        raise ValueError("a_scale must be [M, K/128] and w_scale [N/128, K/128]")
+    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    wsb = fp8_gemm_blockscaled_workspace_bytes(M, N, K)
+    if workspace is None and wsb > 0:
+        workspace = torch.empty((wsb,), dtype=torch.uint8, device=a.device)
+    with torch.cuda.device(a.device):
+        rc = lib().fp8_gemm_blockscaled(
+            _ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(c), M, N, K, _ptr(workspace),
+            workspace.numel() if workspace is not None else 0, ctypes.c_void_p(_stream(a.device)))
+    _check("fp8_gemm_blockscaled", rc)
+    return c
+
+
+def fp8_weight_quant_block(w: torch.Tensor, out=None):
+    """128x128 block quantization of a bf16 weight [N, K]."""
+    _need(w, "w", torch.bfloat16)
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [N, K]")
+    N, K = w.shape
+    if out is None:
+        q = torch.empty((N, K), dtype=E4M3, device=w.device)
+        s = torch.empty((max(N // 128, 1), max(K // 128, 1)), dtype=torch.float32, device=w.device)
+    else:
+        q, s = out
+    with torch.cuda.device(w.device):
+        rc = lib().fp8_weight_quant_block(_ptr(w), N, K, _ptr(q), _ptr(s), ctypes.c_void_p(_stream(w.device)))
+    _check("fp8_weight_quant_block", rc)
+    return q, s
+
+
+def debug_encode_e4m3(v: torch.Tensor, out=None):
+    """Test hook: the library's fp32 -> e4m3 rounding, elementwise."""
+    _need(v, "v", torch.float32)
+    o = out if out is not None else torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    with torch.cuda.device(v.device):
+        rc = lib().fp8bs_debug_encode_e4m3(_ptr(v), _ptr(o), v.numel(), ctypes.c_void_p(_stream(v.device)))
+    _check("fp8bs_debug_encode_e4m3", rc)
+    return o

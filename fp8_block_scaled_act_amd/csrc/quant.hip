@@ -1,0 +1,398 @@
+// Dynamic FP8 (e4m3) quantization kernels for gfx950 and their C entry points.
+//
+//  * fp8_act_quant_block: one fp32 scale per 1x128 block (DeepSeek-V3
+//    act_quant, "How to Profile DeepSeek-V3 Inference Kernels Using Triton
+//    Autotuning", section "Benchmarking the Activation Quantization Kernel").
+//  * fp8_amax_quant_tensor: one scale from the exact amax over the tensor,
+//    with a grid that grows with the input and no single-address atomic
+//    (TensorRT-LLM PR "Size the per-tensor FP8 dynamic-quant amax grid to the
+//    input", sections "Description" and "Correctness").
+//  * fp8_weight_quant_block: one scale per 128x128 weight block.
+//
+// Rule for a group: amax = max|x|, s = fl32(amax/448), q = e4m3(clamp(x/s)).
+// All three are HBM-bound streams: 16-byte loads, reductions in registers via
+// DPP, no LDS on the block path.
+#include "device_common.h"
+#include "host_common.h"
+
+namespace fp8bs {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------------------
+// 1x128 blocks. Eight lanes own one block: lane `sub` holds elements
+// [8*sub, 8*sub+8) and [64+8*sub, 64+8*sub+8), so each 16-byte load
+// instruction of a wave reads eight whole 128-byte halves of blocks. The
+// block amax is a 3-step DPP max inside the 8-lane group.
+// ---------------------------------------------------------------------------
+
+// quantize the 8 bf16 of a uint4 with scale s (and r = 1/s on the fast path)
+template <bool kFast>
+__device__ __forceinline__ uint2 quant8(const uint4 v, float s, float r) {
+  float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = kFast ? div_by_scale(f[i], s, r) : div_ieee(f[i], s);
+  return make_uint2(pack4_e4m3(f[0], f[1], f[2], f[3]), pack4_e4m3(f[4], f[5], f[6], f[7]));
+}
+
+__global__ __launch_bounds__(kThreads) void act_quant_block_kernel(
+    const uint4* __restrict__ x, uint2* __restrict__ q, float* __restrict__ scale,
+    int64_t nblocks) {
+  const int64_t blk = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 3;
+  const int sub = threadIdx.x & 7;
+  if (blk >= nblocks) return;  // whole 8-lane groups leave together
+
+  const uint4 v0 = x[blk * 16 + sub];
+  const uint4 v1 = x[blk * 16 + 8 + sub];
+
+  float m = 0.0f;
+  m = absmax2(v0.x, m); m = absmax2(v0.y, m); m = absmax2(v0.z, m); m = absmax2(v0.w, m);
+  m = absmax2(v1.x, m); m = absmax2(v1.y, m); m = absmax2(v1.z, m); m = absmax2(v1.w, m);
+  const float amax = group8_max(m);
+
+  const float s = div_ieee(amax, kE4m3Max);
+  const bool fast = s >= kFastScaleMin;
+  uint2 o0, o1;
+  if (__builtin_expect(__ballot(!fast) == 0, 1)) {
+    const float r = div_ieee(1.0f, s);
+    o0 = quant8<true>(v0, s, r);
+    o1 = quant8<true>(v1, s, r);
+  } else {
+    o0 = quant8<false>(v0, s, 0.0f);
+    o1 = quant8<false>(v1, s, 0.0f);
+  }
+  if (amax == 0.0f) {  // all-zero block: scale 0, codes 0x00
+    o0 = make_uint2(0u, 0u);
+    o1 = make_uint2(0u, 0u);
+  }
+  q[blk * 16 + sub] = o0;
+  q[blk * 16 + 8 + sub] = o1;
+  if (sub == 0) scale[blk] = s;
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 weight blocks: one workgroup per block. Thread t covers row t/2,
+// columns [64*(t%2), 64*(t%2)+64) as 8 uint4.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void weight_quant_block_kernel(
+    const uint16_t* __restrict__ w, uint8_t* __restrict__ q, float* __restrict__ scale,
+    int64_t K) {
+  __shared__ float wave_max_lds[kThreads / 64];
+  const int64_t kb = K / 128;
+  const int64_t bn = blockIdx.y, bk = blockIdx.x;
+  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int64_t base = (bn * 128 + row) * K + bk * 128 + half * 64;
+  const uint4* src = reinterpret_cast<const uint4*>(w + base);
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = src[i];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    m = absmax2(v[i].x, m); m = absmax2(v[i].y, m);
+    m = absmax2(v[i].z, m); m = absmax2(v[i].w, m);
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) wave_max_lds[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(wave_max_lds[0], wave_max_lds[1]),
+                           fmaxf(wave_max_lds[2], wave_max_lds[3]));
+  const float s = div_ieee(amax, kE4m3Max);
+  uint2 o[8];
+  if (s >= kFastScaleMin) {  // uniform across the workgroup
+    const float r = div_ieee(1.0f, s);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = quant8<true>(v[i], s, r);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = quant8<false>(v[i], s, 0.0f);
+  }
+  if (amax == 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = make_uint2(0u, 0u);
+  }
+  uint4* dst = reinterpret_cast<uint4*>(q + base);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    dst[i] = make_uint4(o[2 * i].x, o[2 * i].y, o[2 * i + 1].x, o[2 * i + 1].y);
+  if (threadIdx.x == 0) scale[bn * kb + bk] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Per-tensor quantization.
+//
+// Small inputs (numel <= kSmallNumel): one workgroup of 1024 threads reads
+// the tensor for the amax, reduces in LDS, then quantizes (the second read
+// hits L2). Large inputs: stage 1 writes one partial max per workgroup to the
+// workspace (grid sized to numel, capped), stage 2 has every workgroup reduce
+// those partials itself before quantizing its share; workgroup 0 writes the
+// scale. No atomics, deterministic.
+// ---------------------------------------------------------------------------
+constexpr int64_t kSmallNumel = 1 << 17;
+constexpr int kMaxPartials = 1024;
+constexpr int kSmallThreads = 1024;
+constexpr int kVecPerThread = 4;  // uint4 (8 bf16) per thread per iteration
+
+__device__ __forceinline__ float tail_absmax(const uint16_t* x, int64_t begin, int64_t end, float m) {
+  for (int64_t i = begin; i < end; ++i)
+    m = fmaxf(m, fabsf(__uint_as_float(static_cast<uint32_t>(x[i]) << 16)));
+  return m;
+}
+
+template <bool kFast>
+__device__ __forceinline__ void tail_quant(const uint16_t* x, uint8_t* q, int64_t begin,
+                                           int64_t end, float s, float r, bool zero) {
+  for (int64_t i = begin; i < end; ++i) {
+    const float f = __uint_as_float(static_cast<uint32_t>(x[i]) << 16);
+    const float y = kFast ? div_by_scale(f, s, r) : div_ieee(f, s);
+    const uint32_t c = pack4_e4m3(y, 0.0f, 0.0f, 0.0f) & 0xFFu;
+    q[i] = zero ? 0 : static_cast<uint8_t>(c);
+  }
+}
+
+template <int kBlock>
+__device__ __forceinline__ float block_max(float m, float* lds) {
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float r = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kBlock / 64; ++i) r = fmaxf(r, lds[i]);
+  return r;
+}
+
+template <bool kFast>
+__device__ __forceinline__ void quant_range(const uint4* xv, uint2* qv, int64_t nvec,
+                                            int64_t first, int64_t stride, float s, float r,
+                                            bool zero) {
+  for (int64_t i = first; i < nvec; i += stride) {
+    uint2 o = quant8<kFast>(xv[i], s, r);
+    if (zero) o = make_uint2(0u, 0u);
+    qv[i] = o;
+  }
+}
+
+__global__ __launch_bounds__(kSmallThreads) void tensor_quant_small_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ scale,
+    int64_t numel) {
+  __shared__ float lds[kSmallThreads / 64];
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const int64_t nvec = numel >> 3;
+  float m = 0.0f;
+  for (int64_t i = threadIdx.x; i < nvec; i += kSmallThreads) {
+    const uint4 v = xv[i];
+    m = absmax2(v.x, m); m = absmax2(v.y, m); m = absmax2(v.z, m); m = absmax2(v.w, m);
+  }
+  if (threadIdx.x == 0) m = tail_absmax(x, nvec << 3, numel, m);
+  const float amax = block_max<kSmallThreads>(m, lds);
+  const float s = div_ieee(amax, kE4m3Max);
+  const bool zero = amax == 0.0f;
+  uint2* qv = reinterpret_cast<uint2*>(q);
+  if (s >= kFastScaleMin) {
+    const float r = div_ieee(1.0f, s);
+    quant_range<true>(xv, qv, nvec, threadIdx.x, kSmallThreads, s, r, zero);
+    if (threadIdx.x == 0) tail_quant<true>(x, q, nvec << 3, numel, s, r, zero);
+  } else {
+    quant_range<false>(xv, qv, nvec, threadIdx.x, kSmallThreads, s, 0.0f, zero);
+    if (threadIdx.x == 0) tail_quant<false>(x, q, nvec << 3, numel, s, 0.0f, zero);
+  }
+  if (threadIdx.x == 0) scale[0] = s;
+}
+
+__global__ __launch_bounds__(kThreads) void tensor_amax_partial_kernel(
+    const uint16_t* __restrict__ x, float* __restrict__ partial, int64_t numel) {
+  __shared__ float lds[kThreads / 64];
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const int64_t nvec = numel >> 3;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  float m = 0.0f;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  for (; i + (kVecPerThread - 1) * stride < nvec; i += kVecPerThread * stride) {
+    uint4 v[kVecPerThread];
+#pragma unroll
+    for (int j = 0; j < kVecPerThread; ++j) v[j] = xv[i + j * stride];
+#pragma unroll
+    for (int j = 0; j < kVecPerThread; ++j) {
+      m = absmax2(v[j].x, m); m = absmax2(v[j].y, m);
+      m = absmax2(v[j].z, m); m = absmax2(v[j].w, m);
+    }
+  }
+  for (; i < nvec; i += stride) {
+    const uint4 v = xv[i];
+    m = absmax2(v.x, m); m = absmax2(v.y, m); m = absmax2(v.z, m); m = absmax2(v.w, m);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) m = tail_absmax(x, nvec << 3, numel, m);
+  m = block_max<kThreads>(m, lds);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+__global__ __launch_bounds__(kThreads) void tensor_apply_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ scale,
+    const float* __restrict__ partial, int npartial, int64_t numel) {
+  __shared__ float lds[kThreads / 64];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < npartial; i += kThreads) m = fmaxf(m, partial[i]);
+  const float amax = block_max<kThreads>(m, lds);
+  const float s = div_ieee(amax, kE4m3Max);
+  const bool zero = amax == 0.0f;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint2* qv = reinterpret_cast<uint2*>(q);
+  const int64_t nvec = numel >> 3;
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  const bool head = blockIdx.x == 0 && threadIdx.x == 0;
+  if (s >= kFastScaleMin) {
+    const float r = div_ieee(1.0f, s);
+    quant_range<true>(xv, qv, nvec, first, stride, s, r, zero);
+    if (head) tail_quant<true>(x, q, nvec << 3, numel, s, r, zero);
+  } else {
+    quant_range<false>(xv, qv, nvec, first, stride, s, 0.0f, zero);
+    if (head) tail_quant<false>(x, q, nvec << 3, numel, s, 0.0f, zero);
+  }
+  if (head) scale[0] = s;
+}
+
+int tensor_grid(int64_t numel, int num_cus) {
+  const int64_t nvec = (numel >> 3) + 1;
+  const int64_t per_wg = static_cast<int64_t>(kThreads) * kVecPerThread;
+  int64_t g = (nvec + per_wg - 1) / per_wg;
+  const int64_t cap = std::min<int64_t>(kMaxPartials, 4LL * num_cus);
+  if (g > cap) g = cap;
+  return static_cast<int>(g < 1 ? 1 : g);
+}
+
+// ---------------------------------------------------------------------------
+// test hook: elementwise fp32 -> e4m3 with the library's conversion
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void debug_encode_kernel(const float4* __restrict__ in,
+                                                                uint32_t* __restrict__ out,
+                                                                int64_t n4) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= n4) return;
+  const float4 v = in[i];
+  out[i] = pack4_e4m3(v.x, v.y, v.z, v.w);
+}
+
+__global__ void debug_encode_tail_kernel(const float* __restrict__ in, uint8_t* __restrict__ out,
+                                         int64_t begin, int64_t n) {
+  const int64_t i = begin + threadIdx.x;
+  if (i < n) out[i] = static_cast<uint8_t>(pack4_e4m3(in[i], 0.0f, 0.0f, 0.0f) & 0xFFu);
+}
+
+}  // namespace
+}  // namespace fp8bs
+
+using namespace fp8bs;
+
+extern "C" {
+
+const char* fp8bs_status_string(int status) {
+  switch (status) {
+    case FP8BS_OK: return "FP8BS_OK";
+    case FP8BS_ERR_NULL: return "FP8BS_ERR_NULL: a required pointer is NULL";
+    case FP8BS_ERR_SHAPE: return "FP8BS_ERR_SHAPE: size out of range or not a multiple of 128";
+    case FP8BS_ERR_ALIGN: return "FP8BS_ERR_ALIGN: pointer not aligned as documented";
+    case FP8BS_ERR_WORKSPACE: return "FP8BS_ERR_WORKSPACE: workspace missing or too small";
+    case FP8BS_ERR_DEVICE: return "FP8BS_ERR_DEVICE: no HIP device or device is not gfx950";
+    case FP8BS_ERR_LAUNCH: return "FP8BS_ERR_LAUNCH: kernel launch failed";
+    default: return "FP8BS_ERR_UNKNOWN";
+  }
+}
+
+int fp8_act_quant_block(const void* x_bf16, int64_t M, int64_t K, void* q_e4m3, float* scale,
+                        void* stream) {
+  if (!x_bf16 || !q_e4m3 || !scale) return FP8BS_ERR_NULL;
+  if (M < 1 || K < 128 || K % 128 != 0) return FP8BS_ERR_SHAPE;
+  if (M > (INT64_MAX / K)) return FP8BS_ERR_SHAPE;
+  if (!aligned(x_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(scale, 4)) return FP8BS_ERR_ALIGN;
+  const DeviceInfo dev = current_device();
+  if (dev.status != FP8BS_OK) return dev.status;
+  const int64_t nblocks = M * (K / 128);
+  const int64_t grid = (nblocks * 8 + kThreads - 1) / kThreads;
+  if (grid > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(act_quant_block_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
+                     as_stream(stream), static_cast<const uint4*>(x_bf16),
+                     static_cast<uint2*>(q_e4m3), scale, nblocks);
+  return launch_status();
+}
+
+int fp8_weight_quant_block(const void* w_bf16, int64_t N, int64_t K, void* q_e4m3, float* scale,
+                           void* stream) {
+  if (!w_bf16 || !q_e4m3 || !scale) return FP8BS_ERR_NULL;
+  if (N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
+  if (N / 128 > 65535 || K / 128 > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  if (!aligned(w_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(scale, 4)) return FP8BS_ERR_ALIGN;
+  const DeviceInfo dev = current_device();
+  if (dev.status != FP8BS_OK) return dev.status;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(weight_quant_block_kernel,
+                     dim3(static_cast<unsigned>(K / 128), static_cast<unsigned>(N / 128)),
+                     dim3(kThreads), 0, as_stream(stream), static_cast<const uint16_t*>(w_bf16),
+                     static_cast<uint8_t*>(q_e4m3), scale, K);
+  return launch_status();
+}
+
+size_t fp8_amax_quant_tensor_workspace_bytes(int64_t numel) {
+  return numel > kSmallNumel ? kMaxPartials * sizeof(float) : 0;
+}
+
+int fp8_amax_quant_tensor(const void* x_bf16, int64_t numel, void* q_e4m3, float* scale,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x_bf16 || !q_e4m3 || !scale) return FP8BS_ERR_NULL;
+  if (numel < 1) return FP8BS_ERR_SHAPE;
+  if (!aligned(x_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(scale, 4)) return FP8BS_ERR_ALIGN;
+  const size_t need = fp8_amax_quant_tensor_workspace_bytes(numel);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return FP8BS_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return FP8BS_ERR_ALIGN;
+  }
+  const DeviceInfo dev = current_device();
+  if (dev.status != FP8BS_OK) return dev.status;
+  hipStream_t st = as_stream(stream);
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  uint8_t* q = static_cast<uint8_t*>(q_e4m3);
+  (void)hipGetLastError();
+  if (numel <= kSmallNumel) {
+    hipLaunchKernelGGL(tensor_quant_small_kernel, dim3(1), dim3(kSmallThreads), 0, st, x, q, scale,
+                       numel);
+    return launch_status();
+  }
+  float* partial = static_cast<float*>(workspace);
+  const int g = tensor_grid(numel, dev.num_cus);
+  hipLaunchKernelGGL(tensor_amax_partial_kernel, dim3(g), dim3(kThreads), 0, st, x, partial,
+                     numel);
+  if (hipGetLastError() != hipSuccess) return FP8BS_ERR_LAUNCH;
+  const int64_t nvec = (numel >> 3) + 1;
+  int64_t ga = (nvec + kThreads * 2 - 1) / (kThreads * 2);
+  ga = std::min<int64_t>(ga, 8LL * dev.num_cus);
+  hipLaunchKernelGGL(tensor_apply_kernel, dim3(static_cast<unsigned>(ga)), dim3(kThreads), 0, st, x,
+                     q, scale, partial, g, numel);
+  return launch_status();
+}
+
+int fp8bs_debug_encode_e4m3(const float* in, void* out, int64_t n, void* stream) {
+  if (!in || !out) return FP8BS_ERR_NULL;
+  if (n < 1) return FP8BS_ERR_SHAPE;
+  if (!aligned(in, 16) || !aligned(out, 16)) return FP8BS_ERR_ALIGN;
+  const DeviceInfo dev = current_device();
+  if (dev.status != FP8BS_OK) return dev.status;
+  const int64_t n4 = n / 4;
+  (void)hipGetLastError();
+  if (n4 > 0) {
+    const int64_t grid = (n4 + kThreads - 1) / kThreads;
+    if (grid > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+    hipLaunchKernelGGL(debug_encode_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
+                       as_stream(stream), reinterpret_cast<const float4*>(in),
+                       static_cast<uint32_t*>(out), n4);
+  }
+  if (n % 4) {
+    hipLaunchKernelGGL(debug_encode_tail_kernel, dim3(1), dim3(4), 0, as_stream(stream), in,
+                       static_cast<uint8_t*>(out), n4 * 4, n);
+  }
+  return launch_status();
+}
+
+}  // extern "C"

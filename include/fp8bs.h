@@ -1,0 +1,145 @@
+/*
+ * fp8bs — FP8 (OCP e4m3) quantize-and-multiply path for AMD MI355X (gfx950).
+ *
+ * C ABI. Every tensor argument is a DEVICE pointer to contiguous, row-major
+ * memory on the current HIP device; sizes are element counts. ``stream`` is a
+ * hipStream_t passed as ``void*`` (NULL = the null stream). Every call only
+ * validates its arguments and enqueues kernels on ``stream``; it never
+ * allocates, frees or synchronizes, and outputs are valid once the stream has
+ * reached the work. The library keeps no mutable state besides a per-device
+ * cache of the device check, so calls from several host threads are safe.
+ *
+ * Ownership: the caller owns every buffer (inputs, outputs and workspaces).
+ * Inputs are read only. Outputs are overwritten entirely and must not alias
+ * an input.
+ *
+ * Errors: a non-zero fp8bs_status is returned BEFORE anything is enqueued for
+ * null pointers, bad sizes, misaligned pointers and too-small workspaces; on a
+ * device that is not gfx950; and, after the enqueue, when the HIP runtime
+ * reports a launch error. fp8bs_status_string() names each code.
+ *
+ * Numerics shared by the quantizers (e4m3 "fn": 1 sign, 4 exponent, 3
+ * mantissa bits, largest finite 448): for a group of bf16 values x
+ *     amax = max |x|                  (exact)
+ *     s    = fl32(amax / 448)         (IEEE binary32 division)
+ *     q    = e4m3_rne(clamp(fl32(x / s), -448, 448))
+ * where e4m3_rne rounds to nearest, ties to even, and keeps the sign of
+ * values that round to zero; a group with amax == 0 gets s = 0 and all codes
+ * 0x00. Inputs must be finite (NaN and Inf are outside the contract). Scale
+ * and codes are bit-for-bit those of this rule.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8BS_OK = 0,
+  FP8BS_ERR_NULL = 1,      /* a required pointer is NULL */
+  FP8BS_ERR_SHAPE = 2,     /* a size is out of range or not a multiple of 128 */
+  FP8BS_ERR_ALIGN = 3,     /* a pointer is not aligned as documented */
+  FP8BS_ERR_WORKSPACE = 4, /* workspace missing or smaller than required */
+  FP8BS_ERR_DEVICE = 5,    /* no HIP device, or the current device is not gfx950 */
+  FP8BS_ERR_LAUNCH = 6     /* the HIP runtime reported an error at launch */
+} fp8bs_status;
+
+/* Name of a status code (static string; never NULL). */
+const char* fp8bs_status_string(int status);
+
+/*
+ * 1x128 block dynamic activation quantization.
+ * DeepSeek-V3 act_quant ("How to Profile DeepSeek-V3 Inference Kernels Using
+ * Triton Autotuning", sections "Understanding the Autotuned Kernels in
+ * DeepSeek-V3" and "Benchmarking the Activation Quantization Kernel"):
+ * block-wise quantization to FP8 with one scaling factor per block of 128.
+ *
+ *   x_bf16  [M, K] bf16, 16-byte aligned           (input)
+ *   q_e4m3  [M, K] e4m3 bytes, 16-byte aligned      (output)
+ *   scale   [M, K/128] fp32, 4-byte aligned         (output)
+ * Block b of row m is x[m, 128b .. 128b+127]; its scale is scale[m, b].
+ * Requires M >= 1, K >= 128, K % 128 == 0 (else FP8BS_ERR_SHAPE).
+ */
+int fp8_act_quant_block(const void* x_bf16, int64_t M, int64_t K,
+                        void* q_e4m3, float* scale, void* stream);
+
+/*
+ * Per-tensor dynamic quantization: one scale from the exact amax over all
+ * numel elements. TensorRT-LLM PR "Size the per-tensor FP8 dynamic-quant amax
+ * grid to the input" (sections "Description" and "Correctness"): an exact
+ * amax reduction with a grid sized to the input, scale = amax / 448, then the
+ * apply step with that scale.
+ *
+ *   x_bf16     [numel] bf16, 16-byte aligned        (input)
+ *   q_e4m3     [numel] e4m3 bytes, 16-byte aligned  (output)
+ *   scale      [1] fp32, 4-byte aligned             (output, written on device)
+ *   workspace  device scratch of at least
+ *              fp8_amax_quant_tensor_workspace_bytes(numel) bytes, 16-byte
+ *              aligned; may be NULL when that size is 0. Its contents on entry
+ *              do not matter; it must not be shared by calls that can run
+ *              concurrently.
+ * Requires numel >= 1 (any value; no multiple-of-128 requirement).
+ */
+size_t fp8_amax_quant_tensor_workspace_bytes(int64_t numel);
+int fp8_amax_quant_tensor(const void* x_bf16, int64_t numel,
+                          void* q_e4m3, float* scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Block-scaled FP8 GEMM with bf16 output: C = A . W^T.
+ * DeepSeek-V3 fp8_gemm_kernel ("How to Profile DeepSeek-V3 Inference Kernels
+ * Using Triton Autotuning", sections "Understanding the Autotuned Kernels in
+ * DeepSeek-V3", "Autotune Configuration Structure" and "Benchmarking the FP8
+ * GEMM Kernel"): FP8 matmul with per-block scaling factors, K consumed in
+ * steps of 128. For every K block b the fp32 accumulator takes
+ *     P_b[m, n] * a_scale[m, b] * w_scale[n/128, b],
+ * P_b being the fp32 dot product of A[m, 128b..] and W[n, 128b..].
+ *
+ *   a_e4m3   [M, K] e4m3, 16-byte aligned           (input, 1x128 blocks)
+ *   a_scale  [M, K/128] fp32, 4-byte aligned        (input)
+ *   w_e4m3   [N, K] e4m3, 16-byte aligned           (input, 128x128 blocks)
+ *   w_scale  [N/128, K/128] fp32, 4-byte aligned    (input)
+ *   c_bf16   [M, N] bf16, 16-byte aligned           (output, RNE from fp32)
+ *   workspace  at least fp8_gemm_blockscaled_workspace_bytes(M, N, K) bytes,
+ *              16-byte aligned (NULL allowed when that size is 0)
+ * Requires M >= 1, N >= 128, K >= 128, N % 128 == 0, K % 128 == 0.
+ * Results agree with the exact product of the dequantized operands within
+ * fp32 accumulation error; the order of the fp32 operations is the
+ * library's own, so results are deterministic but not bit-equal to another
+ * summation order.
+ */
+size_t fp8_gemm_blockscaled_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int fp8_gemm_blockscaled(const void* a_e4m3, const float* a_scale,
+                         const void* w_e4m3, const float* w_scale,
+                         void* c_bf16, int64_t M, int64_t N, int64_t K,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * 128x128 block quantization of a bf16 weight (the "pre-quantized" W that the
+ * GEMM takes: one scale per 128x128 block, same rule as above).
+ *
+ *   w_bf16  [N, K] bf16, 16-byte aligned            (input)
+ *   q_e4m3  [N, K] e4m3, 16-byte aligned            (output)
+ *   scale   [N/128, K/128] fp32, 4-byte aligned     (output)
+ * Requires N, K >= 128 and multiples of 128.
+ */
+int fp8_weight_quant_block(const void* w_bf16, int64_t N, int64_t K,
+                           void* q_e4m3, float* scale, void* stream);
+
+/*
+ * Test hook: the library's own fp32 -> e4m3 rounding step (clamp to +-448,
+ * round to nearest even, sign kept), applied elementwise, so that it can be
+ * checked exhaustively against a reference encoder.
+ *   in [n] fp32 (finite), 16-byte aligned; out [n] bytes, 16-byte aligned.
+ */
+int fp8bs_debug_encode_e4m3(const float* in, void* out, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */

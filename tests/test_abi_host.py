@@ -1,0 +1,115 @@
+"""The C-ABI library on the host: it loads, exports every entry point that
+include/fp8bs.h declares, and rejects bad arguments before touching a device
+(no kernel is launched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import fp8_block_scaled_act_amd as fb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bs.h")
+
+OK, ENULL, ESHAPE, EALIGN, EWS, EDEV = 0, 1, 2, 3, 4, 5
+P = 0x100000          # a fake, 16-byte aligned pointer value (never dereferenced)
+PU = 0x100001         # a misaligned one
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return fb.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert "fp8_act_quant_block" in names and "fp8_gemm_blockscaled" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(fb.EXPORTED_SYMBOLS)
+
+
+def test_status_strings(L):
+    for code in range(7):
+        s = L.fp8bs_status_string(code).decode()
+        assert s.startswith("FP8BS_")
+    assert L.fp8bs_status_string(99).decode() == "FP8BS_ERR_UNKNOWN"
+
+
+def test_act_quant_argument_errors(L):
+    f = L.fp8_act_quant_block
+    assert f(None, 4, 128, P, P, None) == ENULL
+    assert f(P, 4, 128, None, P, None) == ENULL
+    assert f(P, 4, 128, P, None, None) == ENULL
+    assert f(P, 0, 128, P, P, None) == ESHAPE
+    assert f(P, 4, 100, P, P, None) == ESHAPE
+    assert f(P, 4, 0, P, P, None) == ESHAPE
+    assert f(P, -1, 128, P, P, None) == ESHAPE
+    assert f(PU, 4, 128, P, P, None) == EALIGN
+    assert f(P, 4, 128, PU, P, None) == EALIGN
+    assert f(P, 4, 128, P, P + 2, None) == EALIGN
+
+
+def test_tensor_quant_argument_errors(L):
+    f = L.fp8_amax_quant_tensor
+    ws = L.fp8_amax_quant_tensor_workspace_bytes
+    assert ws(1) == 0 and ws(1 << 17) == 0
+    big = 1 << 20
+    assert ws(big) > 0
+    assert f(None, 10, P, P, None, 0, None) == ENULL
+    assert f(P, 0, P, P, None, 0, None) == ESHAPE
+    assert f(PU, 10, P, P, None, 0, None) == EALIGN
+    assert f(P, big, P, P, None, 0, None) == EWS
+    assert f(P, big, P, P, P, ws(big) - 1, None) == EWS
+    assert f(P, big, P, P, PU, ws(big), None) == EALIGN
+
+
+def test_gemm_argument_errors(L):
+    f = L.fp8_gemm_blockscaled
+    assert f(None, P, P, P, P, 4, 128, 128, None, 0, None) == ENULL
+    assert f(P, P, P, None, P, 4, 128, 128, None, 0, None) == ENULL
+    assert f(P, P, P, P, P, 0, 128, 128, None, 0, None) == ESHAPE
+    assert f(P, P, P, P, P, 4, 100, 128, None, 0, None) == ESHAPE
+    assert f(P, P, P, P, P, 4, 128, 64, None, 0, None) == ESHAPE
+    assert f(P, P, P, P, P, 4, 128, 130, None, 0, None) == ESHAPE
+    assert f(PU, P, P, P, P, 4, 128, 128, None, 0, None) == EALIGN
+    assert f(P, P, P, P, PU, 4, 128, 128, None, 0, None) == EALIGN
+    assert f(P, P + 1, P, P, P, 4, 128, 128, None, 0, None) == EALIGN
+
+
+def test_weight_quant_argument_errors(L):
+    f = L.fp8_weight_quant_block
+    assert f(None, 128, 128, P, P, None) == ENULL
+    assert f(P, 64, 128, P, P, None) == ESHAPE
+    assert f(P, 128, 192, P, P, None) == ESHAPE
+    assert f(PU, 128, 128, P, P, None) == EALIGN
+
+
+def test_debug_encode_argument_errors(L):
+    f = L.fp8bs_debug_encode_e4m3
+    assert f(None, P, 4, None) == ENULL
+    assert f(P, P, 0, None) == ESHAPE
+    assert f(PU, P, 4, None) == EALIGN
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path only")
+def test_valid_arguments_without_a_device_report_device_error(L):
+    # all arguments valid: the next step is the device check, which fails here
+    assert L.fp8_act_quant_block(P, 4, 128, P, P, None) == EDEV
+    assert L.fp8_gemm_blockscaled(P, P, P, P, P, 4, 128, 128, None, 0, None) == EDEV
+
+
+def test_python_binding_rejects_bad_tensors():
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)       # CPU tensor
+    with pytest.raises(ValueError):
+        fb.fp8_act_quant_block(x)
+    with pytest.raises(TypeError):
+        fb.fp8_act_quant_block(torch.zeros((4, 128), dtype=torch.float32))

@@ -1,0 +1,152 @@
+"""GPU parity of the block-scaled FP8 GEMM against the fp64 oracle over the
+dequantized operands, through the C ABI.
+
+Operands are quantized by the oracle (never by the GPU). The comparison rule
+(oracle.gemm.compare_gemm): normwise max|C-R|/max|R| <= 1e-2 and elementwise
+|C-R| <= 4 bf16 ulp(R) + (128 + K/128 + 2) * 2**-24 * (|A| . |W|^T).
+The integer-valued case is bit-exact: every fp32 partial sum is an exact
+integer there, so any summation order gives bf16_rne(exact).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import e4m3, gemm, quant
+from tests.helpers import (bf16_to_dev, binding, f32_to_dev, say, to_bf16_bits, u8_to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def operands(a_bits, w_bits, w_scale=None):
+    qa, sa = quant.act_quant_block(a_bits)
+    qw, sw = quant.weight_quant_block(w_bits)
+    if w_scale is not None:
+        sw = np.asarray(w_scale, np.float32)
+    return qa, sa, qw, sw
+
+
+def run_gemm(qa, sa, qw, sw, label):
+    fb = binding()
+    say("gemm_blockscaled", label, qa.shape, qw.shape)
+    c = fb.fp8_gemm_blockscaled(u8_to_dev(qa), f32_to_dev(sa), u8_to_dev(qw), f32_to_dev(sw))
+    torch.cuda.synchronize()
+    return to_bf16_bits(c)
+
+
+def check_full(qa, sa, qw, sw, label):
+    c = run_gemm(qa, sa, qw, sw, label)
+    R = gemm.gemm_blockscaled_ref(qa, sa, qw, sw)
+    S = gemm.gemm_abs_ref(qa, sa, qw, sw)
+    res = gemm.compare_gemm(c, R, S, qa.shape[1])
+    assert res["ok"], (label, res)
+    return res
+
+
+def check_rows(qa, sa, qw, sw, rows, label):
+    c = run_gemm(qa, sa, qw, sw, label)
+    R = gemm.gemm_blockscaled_ref(qa[rows], sa[rows], qw, sw)
+    S = gemm.gemm_abs_ref(qa[rows], sa[rows], qw, sw)
+    res = gemm.compare_gemm(c[rows], R, S, qa.shape[1])
+    assert res["ok"], (label, res)
+    return res
+
+
+def test_c1_tiny():
+    d = synth.gen_c1()
+    check_full(*operands(d["a"], d["w"]), "C1 32x512x512")
+
+
+@pytest.mark.parametrize("M", [1, 8, 32, 64])
+def test_c3_decode(M):
+    d = synth.gen_c3(M)
+    check_full(*operands(d["a"], d["w"]), f"C3 M={M}")
+
+
+def test_c4_prefill_sampled_rows():
+    d = synth.gen_c4()
+    qa, sa, qw, sw = operands(d["a"], d["w"])
+    rows = np.sort(np.random.default_rng(44).choice(qa.shape[0], 192, replace=False))
+    rows = np.unique(np.concatenate([rows, [0, 127, 128, 4095]]))
+    check_rows(qa, sa, qw, sw, rows, "C4 4096x4096x7168")
+
+
+def test_c5_large_m_sampled_rows():
+    d = synth.gen_c5()
+    qa, sa, qw, sw = operands(d["a"], d["w"], d["w_scale"])
+    kb = qa.shape[1] // 128
+    special = np.concatenate([d["zero_blocks"][:16] // kb, d["big_blocks"][:16] // kb])
+    rng = np.random.default_rng(55)
+    rows = np.unique(np.concatenate([rng.choice(qa.shape[0], 160, replace=False), special,
+                                     [0, 16383]]))
+    check_rows(qa, sa, qw, sw, rows, "C5 16384x7168x2048")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (17, 256, 384), (129, 384, 256),
+                                   (200, 128, 1024), (255, 512, 128), (300, 640, 640)])
+def test_ragged_shapes(M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    a = synth.f64_to_bf16_bits(rng.standard_t(3.0, size=(M, K)))
+    w = synth.f64_to_bf16_bits(rng.standard_normal((N, K)) * 0.02)
+    sw = (10.0 ** rng.uniform(-4, -1, size=(N // 128, K // 128))).astype(np.float32)
+    check_full(*operands(a, w, sw), f"ragged {M}x{N}x{K}")
+
+
+INT_CODES = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48}
+
+
+def int_codes(vals):
+    mag = np.vectorize(lambda v: INT_CODES[abs(int(v))])(vals).astype(np.uint8)
+    return mag | np.where(vals < 0, 0x80, 0).astype(np.uint8)
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 7168), (130, 384, 2048)])
+def test_integer_valued_bit_exact(M, N, K):
+    rng = np.random.default_rng(M * N)
+    ia = rng.integers(-4, 5, size=(M, K))
+    iw = rng.integers(-4, 5, size=(N, K))
+    qa, qw = int_codes(ia), int_codes(iw)
+    assert np.array_equal(e4m3.DECODE[qa], ia)
+    sa = np.ones((M, K // 128), np.float32)
+    sw = np.ones((N // 128, K // 128), np.float32)
+    c = run_gemm(qa, sa, qw, sw, f"integer {M}x{N}x{K}")
+    exact = (ia @ iw.T).astype(np.float64)
+    assert np.max(np.abs(exact)) < 2 ** 24
+    assert np.array_equal(c, gemm.f64_to_bf16_rne(exact))
+
+
+def test_identity_weight():
+    rng = np.random.default_rng(8)
+    M, K = 96, 512
+    qa, sa = quant.act_quant_block(synth.f64_to_bf16_bits(rng.standard_normal((M, K))))
+    qw = np.zeros((K, K), np.uint8)
+    np.fill_diagonal(qw, 0x38)
+    sw = np.ones((K // 128, K // 128), np.float32)
+    c = run_gemm(qa, sa, qw, sw, "identity")
+    # C = bf16(dec(qa) * sa): one exact product (e4m3 x fp32 fits in fp32) rounded once
+    want = gemm.f64_to_bf16_rne(gemm.dequant_act(qa, sa))
+    assert np.array_equal(c, want)
+
+
+def test_zero_scales_and_zero_blocks():
+    rng = np.random.default_rng(9)
+    M, N, K = 40, 256, 512
+    a = rng.standard_normal((M, K))
+    a[:, 128:256] = 0.0
+    qa, sa = quant.act_quant_block(synth.f64_to_bf16_bits(a))
+    qw, sw = quant.weight_quant_block(synth.f64_to_bf16_bits(rng.standard_normal((N, K)) * 0.02))
+    sw[1, :] = 0.0
+    c = check_full(qa, sa, qw, sw, "zero scales")
+    out = run_gemm(qa, sa, qw, sw, "zero scales again")
+    assert np.all(out[:, 128:256] & 0x7FFF == 0)
+
+
+def test_deterministic():
+    fb = binding()
+    d = synth.gen_c3(32)
+    qa, sa, qw, sw = operands(d["a"], d["w"])
+    args = (u8_to_dev(qa), f32_to_dev(sa), u8_to_dev(qw), f32_to_dev(sw))
+    c1 = fb.fp8_gemm_blockscaled(*args)
+    c2 = fb.fp8_gemm_blockscaled(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
