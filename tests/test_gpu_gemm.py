@@ -3,7 +3,8 @@ dequantized operands, through the C ABI.
 
 Operands are quantized by the oracle (never by the GPU). The comparison rule
 (oracle.gemm.compare_gemm): normwise max|C-R|/max|R| <= 1e-2 and elementwise
-|C-R| <= 4 bf16 ulp(R) + (128 + K/128 + 2) * 2**-24 * (|A| . |W|^T).
+|C-R| <= 4 bf16 ulp(R) + the accumulation floor of FP8 matrix-core dot
+products plus fp32 scaling and accumulation.
 The integer-valued case is bit-exact: every fp32 partial sum is an exact
 integer there, so any summation order gives bf16_rne(exact).
 """
@@ -38,7 +39,8 @@ def check_full(qa, sa, qw, sw, label):
     c = run_gemm(qa, sa, qw, sw, label)
     R = gemm.gemm_blockscaled_ref(qa, sa, qw, sw)
     S = gemm.gemm_abs_ref(qa, sa, qw, sw)
-    res = gemm.compare_gemm(c, R, S, qa.shape[1])
+    Se = gemm.gemm_exp_envelope_ref(qa, sa, qw, sw)
+    res = gemm.compare_gemm(c, R, S, qa.shape[1], Se)
     assert res["ok"], (label, res)
     return res
 
@@ -47,7 +49,8 @@ def check_rows(qa, sa, qw, sw, rows, label):
     c = run_gemm(qa, sa, qw, sw, label)
     R = gemm.gemm_blockscaled_ref(qa[rows], sa[rows], qw, sw)
     S = gemm.gemm_abs_ref(qa[rows], sa[rows], qw, sw)
-    res = gemm.compare_gemm(c[rows], R, S, qa.shape[1])
+    Se = gemm.gemm_exp_envelope_ref(qa[rows], sa[rows], qw, sw)
+    res = gemm.compare_gemm(c[rows], R, S, qa.shape[1], Se)
     assert res["ok"], (label, res)
     return res
 
@@ -150,3 +153,42 @@ def test_deterministic():
     c2 = fb.fp8_gemm_blockscaled(*args)
     torch.cuda.synchronize()
     assert torch.equal(c1, c2)
+
+
+def model_gemm(qa, sa, qw, sw):
+    """Bit-level model of the kernel's arithmetic: per K block the matrix-core
+    dot product (tests/mfma_model.py), times the fp32 product sa*sw, added into
+    an fp32 accumulator in K order; bf16 rounding at the end. Exact emulation
+    when every scale is a power of two (then each scaled term is exact)."""
+    from tests.mfma_model import block_dot
+    M, K = qa.shape
+    N = qw.shape[0]
+    acc = np.zeros((M, N), np.float32)
+    for b in range(K // 128):
+        P = block_dot(qa[:, None, b * 128:(b + 1) * 128], qw[None, :, b * 128:(b + 1) * 128])
+        cs = (sa[:, b][:, None] * np.repeat(sw[:, b], 128)[None, :]).astype(np.float32)
+        acc = (acc + (P * cs).astype(np.float32)).astype(np.float32)
+    return gemm.f64_to_bf16_rne(acc.astype(np.float64))
+
+
+@pytest.mark.parametrize("dist", ["uniform_codes", "normal", "cancel"])
+def test_bit_exact_against_matrix_core_model(dist):
+    rng = np.random.default_rng({"uniform_codes": 1, "normal": 2, "cancel": 3}[dist])
+    M, N, K = 96, 256, 512
+    fin = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    if dist == "uniform_codes":
+        qa = rng.choice(fin, size=(M, K)); qw = rng.choice(fin, size=(N, K))
+    else:
+        qa = e4m3.encode(np.clip(rng.standard_normal((M, K)) * 60, -448, 448).astype(np.float32))
+        qw = e4m3.encode(np.clip(rng.standard_normal((N, K)) * 60, -448, 448).astype(np.float32))
+        if dist == "cancel":
+            qw[: M] = qa ^ np.uint8(0x80)                 # rows n < M cancel row m = n
+            qw[: M, ::5] = rng.choice(fin, size=(M, K // 5 + 1))[:, : qw[:, ::5].shape[1]]
+    qa = qa.astype(np.uint8); qw = qw.astype(np.uint8)
+    sa = np.ldexp(1.0, rng.integers(-6, 4, size=(M, K // 128))).astype(np.float32)
+    sw = np.ldexp(1.0, rng.integers(-8, 2, size=(N // 128, K // 128))).astype(np.float32)
+    c = run_gemm(qa, sa, qw, sw, f"matrix-core model {dist}")
+    want = model_gemm(qa, sa, qw, sw)
+    bad = np.argwhere(c != want)
+    assert bad.shape[0] == 0, (dist, bad.shape[0], bad[:4].tolist())
+    check_full(qa, sa, qw, sw, f"tolerance {dist}")

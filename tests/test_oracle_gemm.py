@@ -108,24 +108,53 @@ def test_bf16_rounding_matches_torch():
     assert np.array_equal(ours, theirs)
 
 
-def test_compare_accepts_reference_and_rejects_missing_scale():
+def normal_codes(rng, shape, scale):
+    """e4m3 codes of N(0, scale) values (what quantized activations look like)."""
+    v = np.clip(rng.standard_normal(shape) * scale, -448, 448).astype(np.float32)
+    return e4m3.encode(v)
+
+
+def test_compare_accepts_reference_and_rejects_wrong_results():
     rng = np.random.default_rng(6)
     M, N, K = 8, 256, 512
-    qa, qw = rand_codes(rng, (M, K)), rand_codes(rng, (N, K))
+    qa, qw = normal_codes(rng, (M, K), 100.0), normal_codes(rng, (N, K), 100.0)
     sa = (10.0 ** rng.uniform(-2, 0, size=(M, K // 128))).astype(np.float32)
     sw = (10.0 ** rng.uniform(-3, -1, size=(N // 128, K // 128))).astype(np.float32)
     R = gemm.gemm_blockscaled_ref(qa, sa, qw, sw)
     S = gemm.gemm_abs_ref(qa, sa, qw, sw)
+    Se = gemm.gemm_exp_envelope_ref(qa, sa, qw, sw)
     good = gemm.f64_to_bf16_rne(R)
-    res = gemm.compare_gemm(good, R, S, K)
+    res = gemm.compare_gemm(good, R, S, K, Se)
     assert res["ok"], res
+    # one activation block scale lost
     sa_bad = sa.copy(); sa_bad[:, 2] = 1.0
     bad = gemm.f64_to_bf16_rne(gemm.gemm_blockscaled_ref(qa, sa_bad, qw, sw))
-    res = gemm.compare_gemm(bad, R, S, K)
-    assert not res["ok"], res
-    # transposed weight blocks are rejected too
+    assert not gemm.compare_gemm(bad, R, S, K, Se)["ok"]
+    # transposed weight blocks
     bad = gemm.f64_to_bf16_rne(gemm.gemm_blockscaled_ref(qa, sa, qw, sw[::-1]))
-    assert not gemm.compare_gemm(bad, R, S, K)["ok"]
+    assert not gemm.compare_gemm(bad, R, S, K, Se)["ok"]
+    # one K block dropped
+    qa_bad = qa.copy(); qa_bad[:, 128:256] = 0
+    bad = gemm.f64_to_bf16_rne(gemm.gemm_blockscaled_ref(qa_bad, sa, qw, sw))
+    assert not gemm.compare_gemm(bad, R, S, K, Se)["ok"]
+    # a result off by 2**-8 relative everywhere
+    bad = gemm.f64_to_bf16_rne(R * (1 + 2.0 ** -6))
+    assert not gemm.compare_gemm(bad, R, S, K, Se)["ok"]
+
+
+def test_exp_envelope_closed_form():
+    codes = np.arange(256, dtype=np.uint8)
+    env = gemm.exp_envelope(codes)
+    d = np.abs(e4m3.DECODE)
+    fin = np.isfinite(d)
+    normal = fin & (((codes >> 3) & 0xF) > 0)
+    # normal values: 2**e <= |v| < 2**(e+1)
+    assert np.all(env[normal] <= d[normal]) and np.all(d[normal] < 2 * env[normal])
+    # subnormals: envelope 2**-6 above the value; zeros: 0
+    sub = fin & (((codes >> 3) & 0xF) == 0) & ((codes & 0x7) != 0)
+    assert np.all(env[sub] == 2.0 ** -6) and np.all(d[sub] < 2.0 ** -6)
+    assert env[0x00] == 0 and env[0x80] == 0
+    assert env[0x7E] == 256.0 and env[0x38] == 1.0
 
 
 def test_rows_sampler_matches_full():
@@ -137,7 +166,9 @@ def test_rows_sampler_matches_full():
     R = gemm.gemm_blockscaled_ref(qa, sa, qw, sw)
     S = gemm.gemm_abs_ref(qa, sa, qw, sw)
     rows = np.array([0, 5, 3, 3]); cols = np.array([255, 0, 128, 127])
-    r, s = gemm.gemm_rows_ref(qa, sa, qw, sw, rows, cols)
+    Se = gemm.gemm_exp_envelope_ref(qa, sa, qw, sw)
+    r, s, se = gemm.gemm_rows_ref(qa, sa, qw, sw, rows, cols)
     # same sums in another order: equal up to fp64 summation error
     assert np.all(np.abs(r - R[rows, cols]) <= K * 2.0 ** -52 * S[rows, cols])
     assert np.all(np.abs(s - S[rows, cols]) <= K * 2.0 ** -52 * S[rows, cols])
+    assert np.all(np.abs(se - Se[rows, cols]) <= K * 2.0 ** -52 * Se[rows, cols])
