@@ -42,7 +42,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="c5", choices=["c5", "c4", "c3", "c2", "c1"])
+    p.add_argument("--workload", default="c5", choices=["c5", "c4", "c3", "c2", "c1", "copy"],
+                   help="copy: a plain 256 MiB device-to-device copy (HBM reference for counters)")
     p.add_argument("--M", type=int, default=None, help="rows for c2/c3")
     p.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
     p.add_argument("--rotate", type=int, default=3, help="input copies rotated across steps")
@@ -86,6 +87,16 @@ class Workload:
         def bf16(bits):
             t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
             return t.to(dev)
+
+        if w == "copy":
+            nbytes = 256 << 20
+            src = torch.empty((nbytes,), dtype=torch.uint8, device=dev).fill_(1)
+            dst = torch.empty_like(src)
+            self.stages.append(("copy", lambda i: dst.copy_(src), 2 * nbytes, 0))
+            self.config = {"workload": "plain device copy, 256 MiB", "bytes": nbytes}
+            self.M, self.N, self.K = nbytes, 0, 0
+            self.cpu = None
+            return
 
         if w == "c2":
             M = args.M or 65536
@@ -151,48 +162,57 @@ class Workload:
 
 
 def time_steps(torch, wl, steps, warmup, graph):
-    """Warm up, then time exactly `steps` steps; per-stage HIP events on the
-    launch stream (torch's current stream, where the library enqueues)."""
+    """Warm up, then time exactly `steps` steps between two HIP events on the
+    launch stream (torch's current stream, where the library enqueues). Then,
+    for the per-stage figures, time `steps` back-to-back launches of each
+    stage alone the same way (average duration per launch)."""
     st = torch.cuda.current_stream()
-    nst = len(wl.stages)
     for i in range(warmup):
         for _, fn, _, _ in wl.stages:
             fn(i)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    g = None
     if graph:
         g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(st)
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
+        cs = torch.cuda.Stream()
+        cs.wait_stream(st)
+        with torch.cuda.stream(cs):
+            with torch.cuda.graph(g, stream=cs):
                 for i in range(steps):
                     for _, fn, _, _ in wl.stages:
                         fn(i)
         torch.cuda.synchronize()
         g.replay()                                       # one untimed replay
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(st); g.replay(); e1.record(st)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        total_ms = e0.elapsed_time(e1)
-        return total_ms / steps, None, wall
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True); end = torch.cuda.Event(enable_timing=True)
-    start.record(st)
-    for i in range(steps):
-        ev[i][0].record(st)
-        for j, (_, fn, _, _) in enumerate(wl.stages):
-            fn(warmup + i)
-            ev[i][j + 1].record(st)
-    end.record(st)
+    e0, e1 = ev(), ev()
+    e0.record(st)
+    if g is not None:
+        g.replay()
+    else:
+        for i in range(steps):
+            for _, fn, _, _ in wl.stages:
+                fn(warmup + i)
+    e1.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_stage = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(nst)] for i in range(steps)])
-    return start.elapsed_time(end) / steps, per_stage, wall
+    step_ms = e0.elapsed_time(e1) / steps
+
+    per_stage = []
+    for _, fn, _, _ in wl.stages:
+        a, b = ev(), ev()
+        a.record(st)
+        for i in range(steps):
+            fn(i)
+        b.record(st)
+        torch.cuda.synchronize()
+        per_stage.append(a.elapsed_time(b) / steps)
+    return step_ms, per_stage, wall
 
 
 def cpu_baseline(wl, rows_arg):
@@ -207,13 +227,13 @@ def cpu_baseline(wl, rows_arg):
     kind, M, K, N = wl.cpu
     t = 0.0
     if kind == "c2":
-        rows = min(M, rows_arg or 4096)
+        rows = min(M, rows_arg or M)
         x = synth.gen_c2(rows)["x"]
         t0 = time.perf_counter(); oquant.amax_quant_tensor(x); t = time.perf_counter() - t0
         value = (3 * rows * K + 4) / t / 1e9
         return {"value": value, "unit": "GB/s", "cores": 1, "kind": "oracle",
                 "sample": f"per-tensor quant of [{rows}, {K}] bf16 (numpy, one thread), {t:.2f} s"}
-    rows = min(M, rows_arg or {"c5": 2048, "c4": 1024, "c3": M, "c1": M}[kind])
+    rows = min(M, rows_arg or M)
     d = {"c1": lambda: synth.gen_c1(), "c3": lambda: synth.gen_c3(M), "c4": lambda: synth.gen_c4(),
          "c5": lambda: synth.gen_c5()}[kind]()
     a = d["a"][:rows]
@@ -255,10 +275,8 @@ def main():
     for j, (name, _, nbytes, flops) in enumerate(wl.stages):
         e = {"algorithmic_bytes": nbytes}
         if per_stage is not None:
-            us = float(np.mean(per_stage[:, j])) * 1e3
-            e["us_mean"] = us
-            e["us_p10"] = float(np.percentile(per_stage[:, j], 10)) * 1e3
-            e["us_p90"] = float(np.percentile(per_stage[:, j], 90)) * 1e3
+            us = float(per_stage[j]) * 1e3
+            e["us_per_launch"] = us
             e["GB/s"] = nbytes / (us * 1e-6) / 1e9
             e["hbm_frac"] = e["GB/s"] / HBM_PEAK_GBS
             if flops:
@@ -282,7 +300,7 @@ def main():
             roofline = {"bound": "hbm", "achieved": ds["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": ds["GB/s"] / HBM_PEAK_GBS, "traffic": traffic}
         roofline["kernel"] = dominant
-        roofline["us_per_launch"] = ds["us_mean"]
+        roofline["us_per_launch"] = ds["us_per_launch"]
 
     if wl.N:
         value = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
@@ -292,7 +310,7 @@ def main():
         unit = "GB/s"
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and wl.cpu is not None:
         cpu = cpu_baseline(wl, args.cpu_rows)
         cpu["host_cpus"] = os.cpu_count()
         try:
@@ -315,7 +333,8 @@ def main():
         "data": "synthetic (seeded numpy generators; inputs resident in HBM, "
                 f"{max(1, args.rotate)} rotated copies)",
         "config": wl.config,
-        "timing": "HIP graph replay" if args.graph else "HIP events per stage on the launch stream",
+        "timing": ("step: HIP events around all steps" + (" (HIP graph replay)" if args.graph else "")
+                   + "; stages: HIP events around back-to-back launches of each stage"),
         "stages": stages,
         "roofline": roofline,
         "cpu_baseline": cpu,

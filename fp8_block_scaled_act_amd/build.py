@@ -29,6 +29,8 @@ HIPCC_FLAGS = [
     "-shared",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results straight into VGPRs (the scale FMAs read them there)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 
