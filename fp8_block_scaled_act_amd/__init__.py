@@ -35,7 +35,10 @@ __all__ = [
     "EXPORTED_SYMBOLS",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8bs.so")
+# FP8BS_LIB may point at another build of the same library (e.g. to compare
+# kernel variants); by default the library built in this package directory.
+LIB_PATH = os.environ.get("FP8BS_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libfp8bs.so")
 
 EXPORTED_SYMBOLS = (
     "fp8bs_status_string",

@@ -11,10 +11,12 @@
 // Mapping onto CDNA4: one K block of 128 is exactly the K of one
 // v_mfma_f32_16x16x128_f8f6f4, so each MFMA yields the fresh per-block
 // partial P_b of a 16x16 output tile (accumulator input 0) and the scale is
-// applied once per K block with one FMA per output in fp32 registers. W is
-// the MFMA's first operand (16 output rows n) and A the second (16 output
-// columns m): every lane then holds 4 outputs of one activation row m that
-// share a single combined scale a_scale[m,b] * w_scale[n/128,b].
+// applied once per K block with one FMA per output in fp32 registers (the
+// fp32 promotion interval of the DeepSeek-V3 design: the matrix cores' own
+// sum of 128 products is block floating point, see the comparison rule of
+// the tests). W is the MFMA's first operand (16 output rows n) and A the
+// second (16 output columns m): every lane then holds 4 outputs of one
+// activation row m that share a single combined scale.
 #include "device_common.h"
 #include "host_common.h"
 
@@ -27,6 +29,7 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 128;     // K block
+constexpr int kGroupM = 8;   // m tiles walked per n tile (tile order)
 
 __device__ __forceinline__ v4f mfma_16x16x128_fp8(const v8i& a, const v8i& b) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -39,64 +42,6 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
   const bf2 r = __builtin_convertvector(v, bf2);
   return __builtin_bit_cast(uint32_t, r);
 }
-
-// ---------------------------------------------------------------------------
-// Main kernel. Workgroup tile 256 (n) x 128 (m), four waves in a 2 x 2 grid,
-// each wave 128 (n) x 64 (m) = 8 x 4 MFMA tiles of 16 x 16. Per K block a
-// wave issues 32 MFMAs and 128 scale FMAs per lane.
-//
-// Operand tiles and the K block's activation scales go from global memory
-// straight into LDS (global_load_lds, no VGPR staging) in a three-stage ring.
-// A 128-byte tile row holds 8 chunks of 16 bytes; chunk c of row r is stored
-// at position c ^ ((r >> 1) & 7), so the 16 lanes that read one chunk column
-// of 16 consecutive rows touch all 64 banks once. The 128 activation scales
-// of a stage are stored so that each lane's four (rows 16j + lane%16) are
-// adjacent. The weight scale is one scalar load per wave and K block.
-//
-// The MFMAs of MFMA row-tile i are issued before the scale FMAs of row-tile
-// i-1, whose results are complete by then, so the matrix core and the VALU
-// work side by side.
-// ---------------------------------------------------------------------------
-constexpr int kPBN = 256;
-constexpr int kPBM = 128;
-constexpr int kPStages = 3;
-constexpr int kPThreads = 256;
-constexpr int kPWBytes = kPBN * kBK;                           // 32 KiB
-constexpr int kPABytes = kPBM * kBK;                           // 16 KiB
-constexpr int kPSBytes = kPBM * 4;                             // 512 B of scales
-constexpr int kPStageBytes = kPWBytes + kPABytes + kPSBytes;
-constexpr int kPWLoads = kPWBytes / 1024 / 4;                  // per wave: 8
-constexpr int kPALoads = kPABytes / 1024 / 4;                  // per wave: 4
-constexpr int kGroupM = 8;                                     // m tiles walked per n tile
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
-
-__device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row, int c0) {
-  const int x = swz(row);
-  const uint4 lo = *reinterpret_cast<const uint4*>(base + row * 128 + ((c0 ^ x) << 4));
-  const uint4 hi = *reinterpret_cast<const uint4*>(base + row * 128 + (((c0 + 1) ^ x) << 4));
-  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
-
-// waits until at most `n` vector-memory loads of this wave are outstanding
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  // gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
-  __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14));
-}
-
-struct PrefillArgs {
-  const uint8_t* A;
-  const float* sa;
-  const uint8_t* W;
-  const float* sw;
-  uint16_t* C;
-  int64_t M, N, K;
-  int tiles_m, tiles_n;
-};
 
 // Global -> LDS copies (global_load_lds): each lane copies 16 (or 4) bytes
 // from its own address to LDS at lds_base + 16 * lane (or 4 * lane);
@@ -120,12 +65,94 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8_ptr)p));
 }
 
-__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_blockscaled_prefill_kernel(
+// waits until at most `n` vector-memory loads of this wave are outstanding
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  // gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14));
+}
+
+// LDS tile rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row r is
+// stored at position c ^ g(r), g(r) = r2 | r1 << 1 | r3 << 2 (bits of r).
+// A fragment read has lanes 0-15 on chunk c and lanes 16-31 on chunk c+2 of
+// rows 0-15 (and so on): g keeps every group of 32 lanes on distinct 4-byte
+// banks of the 128-bank LDS (measured: the plain (r >> 1) & 7 order left a
+// two-way conflict on every read), and every group of 16 on distinct banks
+// of a 64-bank view as well.
+__device__ __forceinline__ int swz(int row) {
+  return ((row >> 2) & 1) | (row & 2) | (((row >> 3) & 1) << 2);
+}
+
+__device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row, int c0) {
+  const int x = swz(row);
+  const uint4 lo = *reinterpret_cast<const uint4*>(base + row * 128 + ((c0 ^ x) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(base + row * 128 + (((c0 + 1) ^ x) << 4));
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// Scheduling hint for one K block's compute region: per MFMA, up to kDs LDS
+// reads and 4 VALU instructions (the scale FMAs of an earlier MFMA), so the
+// compiler does not hoist all MFMAs ahead of the FMAs that consume them.
+// Masks: 0x008 MFMA, 0x100 DS read, 0x002 VALU.
+template <int kMfma, int kDs>
+__device__ __forceinline__ void interleave_mfma_ds_valu() {
+#pragma unroll
+  for (int k = 0; k < kMfma; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (k < kDs) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled kernel. Workgroup tile BN (n) x BM (m) of WN x WM waves, each wave
+// TN x TM = (BN/WN) x (BM/WM) = NI x NJ MFMA tiles of 16 x 16. Per K block a
+// wave issues NI*NJ MFMAs and 4*NI*NJ scale FMAs per lane.
+//
+// Operand tiles and the K block's activation scales go from global memory
+// straight into LDS in a ring of STAGES stages. Block kb+STAGES-1 is issued
+// right after the barrier that opens block kb, into the stage block kb-1 just
+// left. The activation scales of a stage are laid out so that a lane's NJ
+// scales (rows 16j + lane%16 of its wave's columns) are adjacent. The weight
+// scale is one scalar load per wave and K block (a wave's TN rows sit in one
+// 128-row weight block).
+//
+// The MFMAs of MFMA row i are issued before the scale FMAs of row i-1, whose
+// results are complete by then, so the matrix core and the VALU overlap.
+// ---------------------------------------------------------------------------
+template <int BN, int BM, int WN, int WM, int STAGES>
+struct TileCfg {
+  static constexpr int kWaves = WN * WM;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int TN = BN / WN;
+  static constexpr int TM = BM / WM;
+  static constexpr int NI = TN / 16;
+  static constexpr int NJ = TM / 16;
+  static constexpr int kWBytes = BN * kBK;
+  static constexpr int kABytes = BM * kBK;
+  static constexpr int kSBytes = BM * 4;
+  static constexpr int kStageBytes = kWBytes + kABytes + kSBytes;
+  static constexpr int kWLoads = kWBytes / 1024 / kWaves;   // 1 KiB copies per wave
+  static constexpr int kALoads = kABytes / 1024 / kWaves;
+  static constexpr int kSWaves = BM / 64;                   // waves copying 64 scales each
+  static_assert(kWLoads * 1024 * kWaves == kWBytes && kALoads * 1024 * kWaves == kABytes, "loads");
+  static_assert(kSWaves <= kWaves, "scale copies");
+  static_assert(TN <= 128 && 128 % TN == 0, "a wave's rows must sit in one weight block");
+  static_assert(NJ == 4 || NJ == 2, "scale vector width");
+  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS");
+};
+
+template <int BN, int BM, int WN, int WM, int STAGES, int WAVES_PER_EU>
+__global__ __launch_bounds__(64 * WN * WM) __attribute__((amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
+void gemm_blockscaled_tiled_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, uint16_t* __restrict__ C, int64_t M, int64_t N, int64_t K,
     int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kPStages * kPStageBytes];
+  using T = TileCfg<BN, BM, WN, WM, STAGES>;
+  constexpr int NI = T::NI, NJ = T::NJ;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * T::kStageBytes];
 
   // XCD-aware tile order: the 8 XCDs take workgroups round-robin, so give
   // each XCD one contiguous range of tiles, walked kGroupM m tiles per n tile
@@ -138,122 +165,139 @@ void gemm_blockscaled_prefill_kernel(
   const int gsize = min(tiles_m - first_m, kGroupM);
   const int tm = first_m + (t % (kGroupM * tiles_n)) % gsize;
   const int tn = (t % (kGroupM * tiles_n)) / gsize;
-  const int64_t n0 = static_cast<int64_t>(tn) * kPBN;
-  const int64_t m0 = static_cast<int64_t>(tm) * kPBM;
+  const int64_t n0 = static_cast<int64_t>(tn) * BN;
+  const int64_t m0 = static_cast<int64_t>(tm) * BM;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wn = wave & 1;
-  const int wm = wave >> 1;
+  const int wn = wave % WN;
+  const int wm = wave / WN;
   const int KB = static_cast<int>(K / kBK);
 
-  // --- per-lane global sources of the direct-to-LDS loads (rows clamped to
+  // --- per-lane global sources of the direct-to-LDS copies (rows clamped to
   //     the matrix: rows past M or N load valid memory and are never stored)
   const int lrow8 = lane >> 3;          // row within a 1 KiB slot
   const int lpos = lane & 7;            // physical chunk position
-  const uint8_t* wsrc[kPWLoads];
+  const uint8_t* wsrc[T::kWLoads];
 #pragma unroll
-  for (int i = 0; i < kPWLoads; ++i) {
-    const int row = (wave * kPWLoads + i) * 8 + lrow8;
+  for (int i = 0; i < T::kWLoads; ++i) {
+    const int row = (wave * T::kWLoads + i) * 8 + lrow8;
     const int64_t gr = min<int64_t>(n0 + row, N - 1);
     wsrc[i] = W + gr * K + ((lpos ^ swz(row)) << 4);
   }
-  const uint8_t* asrc[kPALoads];
+  const uint8_t* asrc[T::kALoads];
 #pragma unroll
-  for (int i = 0; i < kPALoads; ++i) {
-    const int row = (wave * kPALoads + i) * 8 + lrow8;
+  for (int i = 0; i < T::kALoads; ++i) {
+    const int row = (wave * T::kALoads + i) * 8 + lrow8;
     const int64_t gr = min<int64_t>(m0 + row, M - 1);
     asrc[i] = A + gr * K + ((lpos ^ swz(row)) << 4);
   }
-  // waves 0 and 1 fetch the scales of m rows [64*wave, 64*wave + 64): lane L
-  // takes row 16*(L%4) + L/4, which lands at LDS float L of that half
-  const bool loads_scales = wave < 2;
-  const float* ssrc = sa + min<int64_t>(m0 + wave * 64 + 16 * (lane & 3) + (lane >> 2), M - 1) * KB;
-
+  // scale slot s = wave*64 + lane (first kSWaves waves) holds the scale of
+  // row wq*TM + 16*j + l16, where s = wq*TM + l16*NJ + j
+  const bool loads_scales = wave < T::kSWaves;
+  const float* ssrc;
+  {
+    const int s = wave * 64 + lane;
+    const int wq = s / T::TM, rem = s % T::TM;
+    const int row = wq * T::TM + 16 * (rem % NJ) + rem / NJ;
+    ssrc = sa + min<int64_t>(m0 + row, M - 1) * KB;
+  }
   // wave-uniform: the weight-scale row address stays in scalar registers
-  const int64_t nb = min<int64_t>((n0 + wn * 128) / 128, N / 128 - 1);
+  const int64_t nb = min<int64_t>((n0 + wn * T::TN) / 128, N / 128 - 1);
   const float* swrow = sw + nb * KB;
 
   const uint32_t lds0 = lds_addr(lds);
   auto issue = [&](int kb) {
-    const uint32_t st = lds0 + (kb % kPStages) * kPStageBytes;
+    const uint32_t st = lds0 + (kb % STAGES) * T::kStageBytes;
 #pragma unroll
-    for (int i = 0; i < kPWLoads; ++i)
-      copy16_to_lds(wsrc[i] + static_cast<int64_t>(kb) * kBK, st + (wave * kPWLoads + i) * 1024);
+    for (int i = 0; i < T::kWLoads; ++i)
+      copy16_to_lds(wsrc[i] + static_cast<int64_t>(kb) * kBK, st + (wave * T::kWLoads + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < kPALoads; ++i)
+    for (int i = 0; i < T::kALoads; ++i)
       copy16_to_lds(asrc[i] + static_cast<int64_t>(kb) * kBK,
-                    st + kPWBytes + (wave * kPALoads + i) * 1024);
-    if (loads_scales) copy4_to_lds(ssrc + kb, st + kPWBytes + kPABytes + wave * 256);
+                    st + T::kWBytes + (wave * T::kALoads + i) * 1024);
+    if (loads_scales) copy4_to_lds(ssrc + kb, st + T::kWBytes + T::kABytes + wave * 256);
   };
 
-  v4f acc[8][4];
+  v4f acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int c0 = 2 * (lane >> 4);
-  const int arow = wm * 64 + (lane & 15);
-  const int wrow = wn * 128 + (lane & 15);
-  issue(0);
-  if (KB > 1) issue(1);
+  const int arow = wm * T::TM + (lane & 15);
+  const int wrow = wn * T::TN + (lane & 15);
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < KB) issue(s);
+  constexpr int kPer = T::kWLoads + T::kALoads;   // copies per block, scale copy aside
   for (int kb = 0; kb < KB; ++kb) {
-    // this wave's copies of block kb (issued two iterations back) are done
-    // once at most the next block's group is outstanding
-    if (kb + 1 < KB) {
-      if (loads_scales) wait_vmcnt<kPWLoads + kPALoads + 1>();
-      else wait_vmcnt<kPWLoads + kPALoads>();
-    } else {
+    // this wave's copies of block kb are done once at most the groups of the
+    // blocks issued after it (STAGES-2 of them, fewer near the end) remain
+    const int ahead = min(KB - 1 - kb, STAGES - 2);
+    if (ahead <= 0) {
       wait_vmcnt<0>();
+    } else if (ahead == 1) {
+      if (loads_scales) wait_vmcnt<kPer + 1>();
+      else wait_vmcnt<kPer>();
+    } else {
+      if (loads_scales) wait_vmcnt<2 * (kPer + 1)>();
+      else wait_vmcnt<2 * kPer>();
     }
     // Plain barrier, no memory fence: every wave's part of block kb is in
     // LDS, and every wave's LDS reads of block kb-1 are complete (they fed
-    // MFMAs already issued), so stage (kb+2)%3 may be refilled.
+    // MFMAs already issued), so that stage may be refilled.
     __builtin_amdgcn_s_barrier();
-    if (kb + 2 < KB) issue(kb + 2);
+    if (kb + STAGES - 1 < KB) issue(kb + STAGES - 1);
 
-    const uint8_t* st = lds + (kb % kPStages) * kPStageBytes;
-    const uint8_t* sA = st + kPWBytes;
-    const float4 sav = *reinterpret_cast<const float4*>(st + kPWBytes + kPABytes + wm * 256 + (lane & 15) * 16);
-    const float swb = swrow[kb];
-    const float cs[4] = {sav.x * swb, sav.y * swb, sav.z * swb, sav.w * swb};
-
-    v8i af[4];
+    const uint8_t* st = lds + (kb % STAGES) * T::kStageBytes;
+    const uint8_t* sA = st + T::kWBytes;
+    v8i af[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) af[j] = lds_frag(sA, arow + j * 16, c0);
-    v4f pp[4], pc[4];
+    for (int j = 0; j < NJ; ++j) af[j] = lds_frag(sA, arow + j * 16, c0);
+    const float* sv = reinterpret_cast<const float*>(st + T::kWBytes + T::kABytes) + wm * T::TM + (lane & 15) * NJ;
+    float cs[NJ];
+    const float swb = swrow[kb];
+    if constexpr (NJ == 4) {
+      const float4 v = *reinterpret_cast<const float4*>(sv);
+      cs[0] = v.x * swb; cs[1] = v.y * swb; cs[2] = v.z * swb; cs[3] = v.w * swb;
+    } else {
+      const float2 v = *reinterpret_cast<const float2*>(sv);
+      cs[0] = v.x * swb; cs[1] = v.y * swb;
+    }
+    v4f pp[NJ], pc[NJ];
     {
       const v8i wf = lds_frag(st, wrow, c0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pp[j] = mfma_16x16x128_fp8(wf, af[j]);
+      for (int j = 0; j < NJ; ++j) pp[j] = mfma_16x16x128_fp8(wf, af[j]);
     }
 #pragma unroll
-    for (int i = 1; i < 8; ++i) {
+    for (int i = 1; i < NI; ++i) {
       const v8i wf = lds_frag(st, wrow + i * 16, c0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pc[j] = mfma_16x16x128_fp8(wf, af[j]);
+      for (int j = 0; j < NJ; ++j) pc[j] = mfma_16x16x128_fp8(wf, af[j]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[i - 1][j][r] = __builtin_fmaf(pp[j][r], cs[j], acc[i - 1][j][r]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pp[j] = pc[j];
+      for (int j = 0; j < NJ; ++j) pp[j] = pc[j];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[7][j][r] = __builtin_fmaf(pp[j][r], cs[j], acc[7][j][r]);
+      for (int r = 0; r < 4; ++r) acc[NI - 1][j][r] = __builtin_fmaf(pp[j][r], cs[j], acc[NI - 1][j][r]);
   }
 
   // epilogue: lane holds D[n = 16i + 4*(lane/16) + r][m = 16j + lane%16]
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t m = m0 + wm * 64 + j * 16 + (lane & 15);
+  for (int j = 0; j < NJ; ++j) {
+    const int64_t m = m0 + wm * T::TM + j * 16 + (lane & 15);
     if (m >= M) continue;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t n = n0 + wn * 128 + i * 16 + (lane >> 4) * 4;
+    for (int i = 0; i < NI; ++i) {
+      const int64_t n = n0 + wn * T::TN + i * 16 + (lane >> 4) * 4;
       if (n >= N) continue;
       uint2 o;
       o.x = bf16x2_rne(acc[i][j][0], acc[i][j][1]);
@@ -261,6 +305,411 @@ void gemm_blockscaled_prefill_kernel(
       *reinterpret_cast<uint2*>(C + m * N + n) = o;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Register-prefetched variant (one wave per SIMD, three LDS stages): the
+// fragments and scales of K block kb+1 are read from LDS while the MFMAs of
+// block kb run, into a second register set, so no MFMA waits for LDS. The
+// barrier that opens iteration kb makes block kb+1 visible; block kb+3 is
+// then copied into the stage block kb left (its fragments are in registers).
+// ---------------------------------------------------------------------------
+template <int NI, int NJ>
+struct Frags {
+  v8i a[NJ];
+  v8i w[NI];
+  float cs[NJ];
+};
+
+template <int BN, int BM, int WN, int WM>
+__global__ __launch_bounds__(64 * WN * WM) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_blockscaled_rp_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
+    const float* __restrict__ sw, uint16_t* __restrict__ C, int64_t M, int64_t N, int64_t K,
+    int tiles_m, int tiles_n) {
+  constexpr int STAGES = 3;
+  using T = TileCfg<BN, BM, WN, WM, STAGES>;
+  constexpr int NI = T::NI, NJ = T::NJ;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * T::kStageBytes];
+
+  const int ntiles = tiles_m * tiles_n;
+  const int per_xcd = (ntiles + 7) / 8;
+  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (t >= ntiles) return;
+  const int group = t / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int tm = first_m + (t % (kGroupM * tiles_n)) % gsize;
+  const int tn = (t % (kGroupM * tiles_n)) / gsize;
+  const int64_t n0 = static_cast<int64_t>(tn) * BN;
+  const int64_t m0 = static_cast<int64_t>(tm) * BM;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave % WN;
+  const int wm = wave / WN;
+  const int KB = static_cast<int>(K / kBK);
+
+  const int lrow8 = lane >> 3;
+  const int lpos = lane & 7;
+  const uint8_t* wsrc[T::kWLoads];
+#pragma unroll
+  for (int i = 0; i < T::kWLoads; ++i) {
+    const int row = (wave * T::kWLoads + i) * 8 + lrow8;
+    const int64_t gr = min<int64_t>(n0 + row, N - 1);
+    wsrc[i] = W + gr * K + ((lpos ^ swz(row)) << 4);
+  }
+  const uint8_t* asrc[T::kALoads];
+#pragma unroll
+  for (int i = 0; i < T::kALoads; ++i) {
+    const int row = (wave * T::kALoads + i) * 8 + lrow8;
+    const int64_t gr = min<int64_t>(m0 + row, M - 1);
+    asrc[i] = A + gr * K + ((lpos ^ swz(row)) << 4);
+  }
+  const bool loads_scales = wave < T::kSWaves;
+  const float* ssrc;
+  {
+    const int s = wave * 64 + lane;
+    const int wq = s / T::TM, rem = s % T::TM;
+    const int row = wq * T::TM + 16 * (rem % NJ) + rem / NJ;
+    ssrc = sa + min<int64_t>(m0 + row, M - 1) * KB;
+  }
+  const int64_t nb = min<int64_t>((n0 + wn * T::TN) / 128, N / 128 - 1);
+  const float* swrow = sw + nb * KB;
+
+  const uint32_t lds0 = lds_addr(lds);
+  auto issue = [&](int kb) {
+    const uint32_t st = lds0 + (kb % STAGES) * T::kStageBytes;
+#pragma unroll
+    for (int i = 0; i < T::kWLoads; ++i)
+      copy16_to_lds(wsrc[i] + static_cast<int64_t>(kb) * kBK, st + (wave * T::kWLoads + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < T::kALoads; ++i)
+      copy16_to_lds(asrc[i] + static_cast<int64_t>(kb) * kBK,
+                    st + T::kWBytes + (wave * T::kALoads + i) * 1024);
+    if (loads_scales) copy4_to_lds(ssrc + kb, st + T::kWBytes + T::kABytes + wave * 256);
+  };
+  constexpr int kPer = T::kWLoads + T::kALoads;
+  // wait until this wave's copies of the block issued `behind` groups ago
+  // have landed (`behind` groups issued after it may remain)
+  auto wait_groups = [&](int behind) {
+    if (behind <= 0) wait_vmcnt<0>();
+    else if (loads_scales) wait_vmcnt<kPer + 1>();
+    else wait_vmcnt<kPer>();
+  };
+
+  const int c0 = 2 * (lane >> 4);
+  const int arow = wm * T::TM + (lane & 15);
+  const int wrow = wn * T::TN + (lane & 15);
+  auto read_frags = [&](Frags<NI, NJ>& f, int kb) {
+    const uint8_t* st = lds + (kb % STAGES) * T::kStageBytes;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) f.a[j] = lds_frag(st + T::kWBytes, arow + j * 16, c0);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) f.w[i] = lds_frag(st, wrow + i * 16, c0);
+    const float* sv = reinterpret_cast<const float*>(st + T::kWBytes + T::kABytes) + wm * T::TM + (lane & 15) * NJ;
+    const float swb = swrow[kb];
+    if constexpr (NJ == 4) {
+      const float4 v = *reinterpret_cast<const float4*>(sv);
+      f.cs[0] = v.x * swb; f.cs[1] = v.y * swb; f.cs[2] = v.z * swb; f.cs[3] = v.w * swb;
+    } else {
+      const float2 v = *reinterpret_cast<const float2*>(sv);
+      f.cs[0] = v.x * swb; f.cs[1] = v.y * swb;
+    }
+  };
+
+  v4f acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](const Frags<NI, NJ>& f) {
+    v4f pp[NJ], pc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) pp[j] = mfma_16x16x128_fp8(f.w[0], f.a[j]);
+#pragma unroll
+    for (int i = 1; i < NI; ++i) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) pc[j] = mfma_16x16x128_fp8(f.w[i], f.a[j]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i - 1][j][r] = __builtin_fmaf(pp[j][r], f.cs[j], acc[i - 1][j][r]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) pp[j] = pc[j];
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[NI - 1][j][r] = __builtin_fmaf(pp[j][r], f.cs[j], acc[NI - 1][j][r]);
+  };
+
+  // one iteration: open block kb+1 (wait, barrier), refill the stage block kb
+  // left with block kb+3, read block kb+1 into `nxt`, compute block kb
+  // an iteration with a next block (kb + 1 < KB)
+  auto step = [&](int kb, const Frags<NI, NJ>& cur, Frags<NI, NJ>& nxt) {
+    wait_groups(kb + 2 < KB ? 1 : 0);
+    __builtin_amdgcn_s_barrier();
+    if (kb + 3 < KB) issue(kb + 3);
+    read_frags(nxt, kb + 1);
+    compute(cur);
+    interleave_mfma_ds_valu<NI * NJ, 2 * (NI + NJ) + 1>();
+  };
+
+  Frags<NI, NJ> f0, f1;
+  issue(0);
+  if (KB > 1) issue(1);
+  wait_groups(KB > 1 ? 1 : 0);
+  __builtin_amdgcn_s_barrier();
+  if (KB > 2) issue(2);
+  read_frags(f0, 0);
+  int kb = 0;
+  for (; kb + 2 < KB; kb += 2) {
+    step(kb, f0, f1);
+    step(kb + 1, f1, f0);
+  }
+  if (kb + 1 < KB) {          // two blocks left: kb (in f0) and kb + 1
+    step(kb, f0, f1);
+    compute(f1);
+  } else {                    // one block left: kb (in f0)
+    compute(f0);
+  }
+
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int64_t m = m0 + wm * T::TM + j * 16 + (lane & 15);
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int64_t n = n0 + wn * T::TN + i * 16 + (lane >> 4) * 4;
+      if (n >= N) continue;
+      uint2 o;
+      o.x = bf16x2_rne(acc[i][j][0], acc[i][j][1]);
+      o.y = bf16x2_rne(acc[i][j][2], acc[i][j][3]);
+      *reinterpret_cast<uint2*>(C + m * N + n) = o;
+    }
+  }
+}
+
+template <int BN, int BM, int WN, int WM>
+int launch_rp(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c,
+              int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const int64_t tiles_m = (M + BM - 1) / BM;
+  const int64_t tiles_n = (N + BN - 1) / BN;
+  const int64_t grid = (tiles_m * tiles_n + 7) / 8 * 8;
+  if (grid > 0x7FFFFFF0LL) return FP8BS_ERR_SHAPE;
+  hipLaunchKernelGGL((gemm_blockscaled_rp_kernel<BN, BM, WN, WM>), dim3(static_cast<unsigned>(grid)),
+                     dim3(64 * WN * WM), 0, st, a, sa, w, sw, c, M, N, K, static_cast<int>(tiles_m),
+                     static_cast<int>(tiles_n));
+  return FP8BS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel (M <= 64): the GEMM is bound by streaming W from HBM, so the
+// work is cut into many pieces of W: workgroup (n tile of 64 rows, K split)
+// has four waves, wave w owning W rows 16w..16w+15 of the tile. Each wave
+// loads its W fragments straight from global memory into registers
+// (kDepth K blocks in flight), the K split's slice of A (at most 64 rows) is
+// staged once in LDS and shared, and each K block is one MFMA per 16
+// activation rows plus the scale FMAs. With more than one K split the fp32
+// partial sums go to the workspace and a second kernel adds them in split
+// order (deterministic) and rounds to bf16.
+// ---------------------------------------------------------------------------
+constexpr int kDecRows = 64;        // W rows per workgroup
+constexpr int kDecDepth = 4;        // K blocks of W in flight per wave
+constexpr int kDecMaxKb = 16;       // K blocks per split (A slice in LDS)
+constexpr int kDecMaxM = 64;
+constexpr int kDecMaxSplits = 32;   // the reduction keeps one float4 per split in flight
+
+// MT: 16-row groups of A (M <= 16*MT); KBMAX: K blocks per split (LDS size)
+template <int MT, int KBMAX>
+__global__ __launch_bounds__(256) void gemm_blockscaled_decode_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
+    const float* __restrict__ sw, uint16_t* __restrict__ C, float* __restrict__ ws, int M, int64_t N,
+    int64_t K, int kb_per, int splits) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[KBMAX * MT * 16 * 128];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kDecRows;
+  const int sp = blockIdx.y;
+  const int KB = static_cast<int>(K / kBK);
+  const int kb0 = sp * kb_per;
+  const int nkb = min(KB - kb0, kb_per);
+  if (nkb <= 0) return;
+
+  // stage A rows [0, 16*MT) x K blocks [kb0, kb0 + nkb) in LDS (rows >= M
+  // read row M-1: valid memory, results never stored), swizzled as in the
+  // tiled kernel
+  constexpr int MP = 16 * MT;
+  for (int id = threadIdx.x; id < nkb * MP * 8; id += 256) {
+    const int kk = id / (MP * 8);
+    const int row = (id / 8) % MP;
+    const int c = id % 8;
+    const int64_t gr = min(row, M - 1);
+    const uint4 v = *reinterpret_cast<const uint4*>(A + gr * K + static_cast<int64_t>(kb0 + kk) * kBK + c * 16);
+    *reinterpret_cast<uint4*>(lds + (kk * MP + row) * 128 + ((c ^ swz(row)) << 4)) = v;
+  }
+
+  const int64_t nrow = n0 + wave * 16 + (lane & 15);          // this lane's W row
+  const uint8_t* wp = W + min<int64_t>(nrow, N - 1) * K + static_cast<int64_t>(kb0) * kBK + 32 * (lane >> 4);
+  const float* swrow = sw + ((n0 + wave * 16) / 128) * KB + kb0;
+  int mrow[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) mrow[j] = min(j * 16 + (lane & 15), M - 1);
+
+  uint4 wq[kDecDepth][2];
+#pragma unroll
+  for (int d = 0; d < kDecDepth; ++d) {
+    if (d < nkb) {
+      wq[d][0] = *reinterpret_cast<const uint4*>(wp + d * kBK);
+      wq[d][1] = *reinterpret_cast<const uint4*>(wp + d * kBK + 16);
+    }
+  }
+  __syncthreads();
+
+  v4f acc[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  const int c0 = 2 * (lane >> 4);
+  for (int kk = 0; kk < nkb; kk += kDecDepth) {
+#pragma unroll
+    for (int d = 0; d < kDecDepth; ++d) {
+      const int k = kk + d;
+      if (k < nkb) {
+        const v8i wf = v8i{(int)wq[d][0].x, (int)wq[d][0].y, (int)wq[d][0].z, (int)wq[d][0].w,
+                           (int)wq[d][1].x, (int)wq[d][1].y, (int)wq[d][1].z, (int)wq[d][1].w};
+        if (k + kDecDepth < nkb) {
+          wq[d][0] = *reinterpret_cast<const uint4*>(wp + (k + kDecDepth) * kBK);
+          wq[d][1] = *reinterpret_cast<const uint4*>(wp + (k + kDecDepth) * kBK + 16);
+        }
+        const float swb = swrow[k];
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+          const v8i af = lds_frag(lds + k * MP * 128, j * 16 + (lane & 15), c0);
+          const v4f p = mfma_16x16x128_fp8(wf, af);
+          const float cs = sa[static_cast<int64_t>(mrow[j]) * KB + kb0 + k] * swb;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(p[r], cs, acc[j][r]);
+        }
+      }
+    }
+  }
+
+  // lane holds D[n = 16*wave + 4*(lane/16) + r][m = 16j + lane%16]
+  const int64_t n = n0 + wave * 16 + (lane >> 4) * 4;
+  if (n >= N) return;
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    const int m = j * 16 + (lane & 15);
+    if (m >= M) continue;
+    if (splits == 1) {
+      uint2 o;
+      o.x = bf16x2_rne(acc[j][0], acc[j][1]);
+      o.y = bf16x2_rne(acc[j][2], acc[j][3]);
+      *reinterpret_cast<uint2*>(C + m * N + n) = o;
+    } else {
+      *reinterpret_cast<float4*>(ws + (static_cast<int64_t>(sp) * M + m) * N + n) =
+          make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+    }
+  }
+}
+
+// C[m, n..n+3] = bf16(sum over splits s = 0, 1, ... of ws[s][m][n..n+3])
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __restrict__ ws,
+                                                                  uint16_t* __restrict__ C,
+                                                                  int64_t mn4, int splits) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= mn4) return;
+  const float4* p = reinterpret_cast<const float4*>(ws) + i;
+  float4 v[kDecMaxSplits];                 // all loads in flight, then added in split order
+#pragma unroll
+  for (int k = 0; k < kDecMaxSplits; ++k)
+    if (k < splits) v[k] = p[k * mn4];
+  float4 s = v[0];
+#pragma unroll
+  for (int k = 1; k < kDecMaxSplits; ++k)
+    if (k < splits) { s.x += v[k].x; s.y += v[k].y; s.z += v[k].z; s.w += v[k].w; }
+  uint2 o;
+  o.x = bf16x2_rne(s.x, s.y);
+  o.y = bf16x2_rne(s.z, s.w);
+  reinterpret_cast<uint2*>(C)[i] = o;
+}
+
+struct DecodePlan {
+  int kb_per;
+  int splits;
+};
+
+// K split for the decode kernel: enough workgroups to keep ~512 in flight,
+// at most kDecMaxKb K blocks per split
+inline DecodePlan decode_plan(int64_t N, int64_t K) {
+  const int64_t KB = K / kBK;
+  const int64_t ntiles = (N + kDecRows - 1) / kDecRows;
+  int64_t want = (512 + ntiles - 1) / ntiles;
+  want = std::max<int64_t>(want, (KB + kDecMaxKb - 1) / kDecMaxKb);
+  want = std::min<int64_t>(want, KB);
+  int kb_per = static_cast<int>((KB + want - 1) / want);
+  kb_per = std::max(1, std::min(kb_per, kDecMaxKb));
+  // at most kDecMaxSplits splits (raises K blocks per split; K beyond
+  // kDecMaxSplits * kDecMaxKb blocks is rejected by the entry point)
+  kb_per = std::max<int>(kb_per, static_cast<int>((KB + kDecMaxSplits - 1) / kDecMaxSplits));
+  const int splits = static_cast<int>((KB + kb_per - 1) / kb_per);
+  return {kb_per, splits};
+}
+
+inline bool use_decode(int64_t M) { return M <= kDecMaxM; }
+
+size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const DecodePlan p = decode_plan(N, K);
+  return p.splits > 1 ? static_cast<size_t>(p.splits) * M * N * sizeof(float) : 0;
+}
+
+int launch_decode(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c,
+                  float* ws, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const DecodePlan p = decode_plan(N, K);
+  const dim3 grid(static_cast<unsigned>((N + kDecRows - 1) / kDecRows), static_cast<unsigned>(p.splits));
+  const int m = static_cast<int>(M);
+  const int mt = (m + 15) / 16;
+#define FP8BS_DEC(MT, KBM)                                                                      \
+  hipLaunchKernelGGL((gemm_blockscaled_decode_kernel<MT, KBM>), grid, dim3(256), 0, st, a, sa, w, \
+                     sw, c, ws, m, N, K, p.kb_per, p.splits)
+#define FP8BS_DEC_KB(MT)                      \
+  if (p.kb_per <= 4) FP8BS_DEC(MT, 4);        \
+  else if (p.kb_per <= 8) FP8BS_DEC(MT, 8);   \
+  else FP8BS_DEC(MT, 16);
+  switch (mt) {
+    case 1: FP8BS_DEC_KB(1) break;
+    case 2: FP8BS_DEC_KB(2) break;
+    case 3: FP8BS_DEC_KB(3) break;
+    default: FP8BS_DEC_KB(4) break;
+  }
+#undef FP8BS_DEC_KB
+#undef FP8BS_DEC
+  if (p.splits > 1) {
+    if (hipGetLastError() != hipSuccess) return FP8BS_ERR_LAUNCH;
+    const int64_t mn4 = M * N / 4;
+    hipLaunchKernelGGL(gemm_splitk_reduce_kernel, dim3(static_cast<unsigned>((mn4 + 255) / 256)), dim3(256), 0, st,
+                       ws, c, mn4, p.splits);
+  }
+  return FP8BS_OK;
+}
+
+#ifndef FP8BS_GEMM_TILE
+#define FP8BS_GEMM_TILE 0
+#endif
+
+template <int BN, int BM, int WN, int WM, int STAGES, int WPE>
+int launch_tiled(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c,
+                 int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const int64_t tiles_m = (M + BM - 1) / BM;
+  const int64_t tiles_n = (N + BN - 1) / BN;
+  const int64_t grid = (tiles_m * tiles_n + 7) / 8 * 8;
+  if (grid > 0x7FFFFFF0LL) return FP8BS_ERR_SHAPE;
+  hipLaunchKernelGGL((gemm_blockscaled_tiled_kernel<BN, BM, WN, WM, STAGES, WPE>),
+                     dim3(static_cast<unsigned>(grid)), dim3(64 * WN * WM), 0, st, a, sa, w, sw, c,
+                     M, N, K, static_cast<int>(tiles_m), static_cast<int>(tiles_n));
+  return FP8BS_OK;
 }
 
 }  // namespace
@@ -271,8 +720,8 @@ using namespace fp8bs;
 extern "C" {
 
 size_t fp8_gemm_blockscaled_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  (void)M; (void)N; (void)K;
-  return 0;
+  if (M < 1 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return 0;
+  return use_decode(M) ? decode_workspace_bytes(M, N, K) : 0;
 }
 
 int fp8_gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m3,
@@ -281,7 +730,8 @@ int fp8_gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w
   if (!a_e4m3 || !a_scale || !w_e4m3 || !w_scale || !c_bf16) return FP8BS_ERR_NULL;
   if (M < 1 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
   if (M > (INT64_MAX / K) || M > (INT64_MAX / N) || N > (INT64_MAX / K)) return FP8BS_ERR_SHAPE;
-  if ((M + 127) / 128 * ((N + 255) / 256) > 0x7FFFFFF0LL || K / 128 > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  if (K / 128 > 0x7FFFFFFF || (M + 127) / 128 > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  if (use_decode(M) && K / 128 > static_cast<int64_t>(kDecMaxSplits) * kDecMaxKb) return FP8BS_ERR_SHAPE;
   if (!aligned(a_e4m3, 16) || !aligned(w_e4m3, 16) || !aligned(c_bf16, 16) ||
       !aligned(a_scale, 4) || !aligned(w_scale, 4))
     return FP8BS_ERR_ALIGN;
@@ -289,15 +739,35 @@ int fp8_gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w
   if (need > 0 && (!workspace || workspace_bytes < need)) return FP8BS_ERR_WORKSPACE;
   const DeviceInfo dev = current_device();
   if (dev.status != FP8BS_OK) return dev.status;
+  const uint8_t* a = static_cast<const uint8_t*>(a_e4m3);
+  const uint8_t* w = static_cast<const uint8_t*>(w_e4m3);
+  uint16_t* c = static_cast<uint16_t*>(c_bf16);
+  hipStream_t st = as_stream(stream);
   (void)hipGetLastError();
-  const int64_t tiles_m = (M + kPBM - 1) / kPBM;
-  const int64_t tiles_n = (N + kPBN - 1) / kPBN;
-  const int64_t grid = (tiles_m * tiles_n + 7) / 8 * 8;
-  hipLaunchKernelGGL(gemm_blockscaled_prefill_kernel, dim3(static_cast<unsigned>(grid)),
-                     dim3(kPThreads), 0, as_stream(stream), static_cast<const uint8_t*>(a_e4m3),
-                     a_scale, static_cast<const uint8_t*>(w_e4m3), w_scale,
-                     static_cast<uint16_t*>(c_bf16), M, N, K, static_cast<int>(tiles_m),
-                     static_cast<int>(tiles_n));
+  int rc;
+  if (use_decode(M)) {
+    rc = launch_decode(a, a_scale, w, w_scale, c, static_cast<float*>(workspace), M, N, K, st);
+    if (rc != FP8BS_OK) return rc;
+    return launch_status();
+  }
+#if FP8BS_GEMM_TILE == 0
+  // 256 x 256 tiles (eight waves, two per SIMD) when they fill the chip,
+  // else 128 x 128 tiles (two workgroups per CU)
+  const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles256 >= dev.num_cus)
+    rc = launch_tiled<256, 256, 2, 4, 2, 2>(a, a_scale, w, w_scale, c, M, N, K, st);
+  else
+    rc = launch_tiled<128, 128, 2, 2, 2, 2>(a, a_scale, w, w_scale, c, M, N, K, st);
+#elif FP8BS_GEMM_TILE == 1
+  rc = launch_tiled<128, 128, 2, 2, 2, 2>(a, a_scale, w, w_scale, c, M, N, K, st);
+#elif FP8BS_GEMM_TILE == 2
+  rc = launch_tiled<256, 256, 2, 4, 2, 2>(a, a_scale, w, w_scale, c, M, N, K, st);
+#elif FP8BS_GEMM_TILE == 3
+  rc = launch_tiled<256, 128, 2, 2, 3, 1>(a, a_scale, w, w_scale, c, M, N, K, st);
+#elif FP8BS_GEMM_TILE == 4
+  rc = launch_rp<256, 128, 2, 2>(a, a_scale, w, w_scale, c, M, N, K, st);
+#endif
+  if (rc != FP8BS_OK) return rc;
   return launch_status();
 }
 

@@ -113,3 +113,8 @@ def test_python_binding_rejects_bad_tensors():
         fb.fp8_act_quant_block(x)
     with pytest.raises(TypeError):
         fb.fp8_act_quant_block(torch.zeros((4, 128), dtype=torch.float32))
+
+
+def test_gemm_decode_k_limit(L):
+    # M <= 64 splits K into at most 32 parts of at most 16 blocks
+    assert L.fp8_gemm_blockscaled(P, P, P, P, P, 8, 128, 128 * 513, None, 0, None) == ESHAPE

@@ -192,3 +192,32 @@ def test_bit_exact_against_matrix_core_model(dist):
     bad = np.argwhere(c != want)
     assert bad.shape[0] == 0, (dist, bad.shape[0], bad[:4].tolist())
     check_full(qa, sa, qw, sw, f"tolerance {dist}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (5, 256, 1024), (16, 2048, 7168), (17, 384, 2048),
+                                   (33, 640, 4096), (64, 2048, 7168), (64, 128, 128 * 40), (48, 7168, 2048)])
+def test_decode_shapes(M, N, K):
+    # M <= 64 runs the W-streaming split-K path: several K splits, fp32
+    # partials in the workspace, reduced in split order
+    rng = np.random.default_rng(M * 7 + N + K)
+    a = synth.f64_to_bf16_bits(rng.standard_normal((M, K)) * 3)
+    w = synth.f64_to_bf16_bits(rng.standard_normal((N, K)) * 0.02)
+    check_full(*operands(a, w), f"decode {M}x{N}x{K}")
+
+
+def test_decode_workspace_size_and_reuse():
+    fb = binding()
+    M, N, K = 8, 2048, 7168
+    wsb = fb.fp8_gemm_blockscaled_workspace_bytes(M, N, K)
+    assert wsb % (M * N * 4) == 0 and wsb >= M * N * 4
+    assert fb.fp8_gemm_blockscaled_workspace_bytes(4096, N, K) == 0
+    d = synth.gen_c3(8)
+    qa, sa, qw, sw = operands(d["a"], d["w"])
+    args = (u8_to_dev(qa), f32_to_dev(sa), u8_to_dev(qw), f32_to_dev(sw))
+    ws = torch.full((wsb,), 0x7F, dtype=torch.uint8, device="cuda:0")     # garbage on entry
+    c1 = fb.fp8_gemm_blockscaled(*args, workspace=ws)
+    c2 = fb.fp8_gemm_blockscaled(*args, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+    with pytest.raises(fb.Fp8bsError):
+        fb.fp8_gemm_blockscaled(*args, workspace=ws[: wsb - 4])
