@@ -232,6 +232,11 @@ void gemm_blockscaled_tiled_kernel(
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < KB) issue(s);
   constexpr int kPer = T::kWLoads + T::kALoads;   // copies per block, scale copy aside
+  // The weight scale of block kb+1 is loaded (scalar load) after the last
+  // fragment read of block kb and waited for right after the next barrier,
+  // before the first fragment read: scalar loads complete out of order, so
+  // while one is in flight every wait for an LDS read is a full wait.
+  float swb = swrow[0];
   for (int kb = 0; kb < KB; ++kb) {
     // this wave's copies of block kb are done once at most the groups of the
     // blocks issued after it (STAGES-2 of them, fewer near the end) remain
@@ -250,33 +255,44 @@ void gemm_blockscaled_tiled_kernel(
     // MFMAs already issued), so that stage may be refilled.
     __builtin_amdgcn_s_barrier();
     if (kb + STAGES - 1 < KB) issue(kb + STAGES - 1);
+    asm volatile("" ::"s"(swb));
+    __builtin_amdgcn_sched_barrier(0);
 
     const uint8_t* st = lds + (kb % STAGES) * T::kStageBytes;
     const uint8_t* sA = st + T::kWBytes;
+    // Block prologue in the order the MFMAs need it: the activation scales,
+    // W row 0 and A column 0 first (the first MFMA waits only for those),
+    // the other fragments behind it.
+    v4f pp[NJ], pc[NJ];
     v8i af[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) af[j] = lds_frag(sA, arow + j * 16, c0);
     const float* sv = reinterpret_cast<const float*>(st + T::kWBytes + T::kABytes) + wm * T::TM + (lane & 15) * NJ;
-    float cs[NJ];
-    const float swb = swrow[kb];
+    float sav[NJ];
     if constexpr (NJ == 4) {
       const float4 v = *reinterpret_cast<const float4*>(sv);
-      cs[0] = v.x * swb; cs[1] = v.y * swb; cs[2] = v.z * swb; cs[3] = v.w * swb;
+      sav[0] = v.x; sav[1] = v.y; sav[2] = v.z; sav[3] = v.w;
     } else {
       const float2 v = *reinterpret_cast<const float2*>(sv);
-      cs[0] = v.x * swb; cs[1] = v.y * swb;
+      sav[0] = v.x; sav[1] = v.y;
     }
-    v4f pp[NJ], pc[NJ];
-    {
-      const v8i wf = lds_frag(st, wrow, c0);
+    v8i wcur = lds_frag(st, wrow, c0);
+    af[0] = lds_frag(sA, arow, c0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) pp[j] = mfma_16x16x128_fp8(wf, af[j]);
-    }
+    for (int j = 1; j < NJ; ++j) af[j] = lds_frag(sA, arow + j * 16, c0);
+    v8i wnext = lds_frag(st, wrow + 16, c0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) pp[j] = mfma_16x16x128_fp8(wcur, af[j]);
+    float cs[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) cs[j] = sav[j] * swb;
+    // W fragments double-buffered: the fragment of row i+1 is read before
+    // the MFMAs of row i, so its LDS latency hides behind NJ MFMAs
 #pragma unroll
     for (int i = 1; i < NI; ++i) {
-      const v8i wf = lds_frag(st, wrow + i * 16, c0);
+      wcur = wnext;
+      if (i + 1 < NI) wnext = lds_frag(st, wrow + (i + 1) * 16, c0);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) pc[j] = mfma_16x16x128_fp8(wf, af[j]);
+      for (int j = 0; j < NJ; ++j) pc[j] = mfma_16x16x128_fp8(wcur, af[j]);
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -288,22 +304,56 @@ void gemm_blockscaled_tiled_kernel(
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[NI - 1][j][r] = __builtin_fmaf(pp[j][r], cs[j], acc[NI - 1][j][r]);
-  }
-
-  // epilogue: lane holds D[n = 16i + 4*(lane/16) + r][m = 16j + lane%16]
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int64_t m = m0 + wm * T::TM + j * 16 + (lane & 15);
-    if (m >= M) continue;
+    __builtin_amdgcn_sched_barrier(0);
+    swb = swrow[min(kb + 1, KB - 1)];
+#ifdef FP8BS_SCHED_HINT
+    // order: A fragments, scales, W rows 0 and 1 first; then per MFMA row i
+    // the next W fragment (2 reads) and NJ x (1 MFMA + 4 VALU)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NJ + 1 + 4, 0);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int64_t n = n0 + wn * T::TN + i * 16 + (lane >> 4) * 4;
-      if (n >= N) continue;
+      if (i >= 1 && i + 1 < NI) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+    }
+#endif
+  }
+
+  // Epilogue through LDS, so that every global store writes whole rows of C.
+  // Lane holds D[n = 16i + 4*(lane/16) + r][m = 16j + lane%16] of the wave's
+  // sub-tile; the bf16 tile is staged row-major (m rows of BN values) in the
+  // ring, 16-byte chunk c of row m stored at chunk c ^ (m & 15), which keeps
+  // the 8-byte writes of a half-wave (16 rows, one chunk pair) and the
+  // 16-byte row reads free of bank conflicts.
+  static_assert(BM * BN * 2 <= STAGES * T::kStageBytes, "C tile must fit the LDS ring");
+  constexpr int kRowBytes = BN * 2;
+  constexpr int kChunks = BN / 8;
+  __syncthreads();   // every wave is done reading the last stage
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int ml = wm * T::TM + j * 16 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int nl = wn * T::TN + i * 16 + (lane >> 4) * 4;
+      const int off = ml * kRowBytes + (((nl >> 3) ^ (ml & 15)) << 4) + ((nl & 4) << 1);
       uint2 o;
       o.x = bf16x2_rne(acc[i][j][0], acc[i][j][1]);
       o.y = bf16x2_rne(acc[i][j][2], acc[i][j][3]);
-      *reinterpret_cast<uint2*>(C + m * N + n) = o;
+      *reinterpret_cast<uint2*>(lds + off) = o;
     }
+  }
+  __syncthreads();
+  static_assert(BM * kChunks % T::kThreads == 0, "row chunks per thread");
+#pragma unroll
+  for (int k = 0; k < BM * kChunks / T::kThreads; ++k) {
+    const int idx = k * T::kThreads + static_cast<int>(threadIdx.x);
+    const int ml = idx / kChunks, c = idx % kChunks;
+    const uint4 v = *reinterpret_cast<const uint4*>(lds + ml * kRowBytes + ((c ^ (ml & 15)) << 4));
+    const int64_t m = m0 + ml, n = n0 + c * 8;
+    if (m < M && n < N) *reinterpret_cast<uint4*>(C + m * N + n) = v;
   }
 }
 
