@@ -17,9 +17,14 @@
 // the tests). W is the MFMA's first operand (16 output rows n) and A the
 // second (16 output columns m): every lane then holds 4 outputs of one
 // activation row m that share a single combined scale.
+#include <type_traits>
+
 #include "device_common.h"
 #include "host_common.h"
 
+#ifndef FP8BS_DMA_ROWS
+#define FP8BS_DMA_ROWS 4
+#endif
 namespace fp8bs {
 namespace {
 
@@ -43,19 +48,37 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Global -> LDS copies (global_load_lds): each lane copies 16 (or 4) bytes
-// from its own address to LDS at lds_base + 16 * lane (or 4 * lane);
-// lds_base is wave-uniform. Issued from inline assembly so that the
-// compiler's wait insertion does not treat every later LDS read as
-// dependent on every copy in flight (it cannot tell the ring stages apart and
-// would wait for all of them); the kernel waits on vmcnt and barriers itself.
-// The instruction writes no VGPR, so no register is left in flight.
-__device__ __forceinline__ void copy16_to_lds(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base)
+// Buffer resource (V#) of a raw byte buffer: base address, size in bytes
+// (num_records, stride 0), 32-bit data format. Loads at offsets at or past
+// the size return zeros instead of touching memory. All four words are
+// wave-uniform and live in scalar registers.
+typedef int v4i_rsrc __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i_rsrc make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  v4i_rsrc r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+// Buffer -> LDS copies (buffer_load ... lds): each lane copies 16 (or 4)
+// bytes at its byte offset `voff` into the buffer to LDS at
+// lds_base + 16 * lane (or 4 * lane); lds_base is wave-uniform. Issued from
+// inline assembly so that the compiler's wait insertion does not treat every
+// later LDS read as dependent on every copy in flight (it cannot tell the
+// ring stages apart and would wait for all of them); the kernel waits on
+// vmcnt and barriers itself. The instruction writes no VGPR, so no register
+// is left in flight. The offset is the only per-lane operand, and the range
+// check replaces any clamping of rows past the end of a matrix.
+__device__ __forceinline__ void copy16_buf_to_lds(uint32_t voff, v4i_rsrc rsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(lds_base)
                : "memory", "m0");
 }
-__device__ __forceinline__ void copy4_to_lds(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_base)
+__device__ __forceinline__ void copy4_buf_to_lds(uint32_t voff, v4i_rsrc rsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(lds_base)
                : "memory", "m0");
 }
 
@@ -91,35 +114,24 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row, int c0) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-// Scheduling hint for one K block's compute region: per MFMA, up to kDs LDS
-// reads and 4 VALU instructions (the scale FMAs of an earlier MFMA), so the
-// compiler does not hoist all MFMAs ahead of the FMAs that consume them.
-// Masks: 0x008 MFMA, 0x100 DS read, 0x002 VALU.
-template <int kMfma, int kDs>
-__device__ __forceinline__ void interleave_mfma_ds_valu() {
-#pragma unroll
-  for (int k = 0; k < kMfma; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (k < kDs) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Tiled kernel. Workgroup tile BN (n) x BM (m) of WN x WM waves, each wave
 // TN x TM = (BN/WN) x (BM/WM) = NI x NJ MFMA tiles of 16 x 16. Per K block a
 // wave issues NI*NJ MFMAs and 4*NI*NJ scale FMAs per lane.
 //
 // Operand tiles and the K block's activation scales go from global memory
-// straight into LDS in a ring of STAGES stages. Block kb+STAGES-1 is issued
-// right after the barrier that opens block kb, into the stage block kb-1 just
-// left. The activation scales of a stage are laid out so that a lane's NJ
-// scales (rows 16j + lane%16 of its wave's columns) are adjacent. The weight
-// scale is one scalar load per wave and K block (a wave's TN rows sit in one
-// 128-row weight block).
+// straight into LDS (buffer loads with the LDS bit) in a ring of STAGES
+// stages. The copies of block kb+STAGES-1 go into the stage block kb-1 left;
+// they are spread over the first MFMA rows of block kb rather than issued in
+// one burst. The activation scales of a stage are laid out so that a lane's
+// NJ scales (rows 16j + lane%16 of its wave's columns) are adjacent. The
+// weight scale is one scalar load per wave and K block (a wave's TN rows sit
+// in one 128-row weight block).
 //
 // The MFMAs of MFMA row i are issued before the scale FMAs of row i-1, whose
-// results are complete by then, so the matrix core and the VALU overlap.
+// results are complete by then, so the matrix core and the VALU overlap. The
+// last MFMA row of a block is issued after the next block's barrier, while
+// that block's first fragment reads are in flight.
 // ---------------------------------------------------------------------------
 template <int BN, int BM, int WN, int WM, int STAGES>
 struct TileCfg {
@@ -174,49 +186,64 @@ void gemm_blockscaled_tiled_kernel(
   const int wm = wave / WN;
   const int KB = static_cast<int>(K / kBK);
 
-  // --- per-lane global sources of the direct-to-LDS copies (rows clamped to
-  //     the matrix: rows past M or N load valid memory and are never stored)
+  // --- copy sources: per-lane 32-bit byte offsets into buffers that start
+  //     at the tile's first row and end at the matrix's last row (rows past
+  //     M or N read as zeros; their outputs are never stored)
   const int lrow8 = lane >> 3;          // row within a 1 KiB slot
   const int lpos = lane & 7;            // physical chunk position
-  const uint8_t* wsrc[T::kWLoads];
+  uint32_t woff[T::kWLoads];
 #pragma unroll
   for (int i = 0; i < T::kWLoads; ++i) {
     const int row = (wave * T::kWLoads + i) * 8 + lrow8;
-    const int64_t gr = min<int64_t>(n0 + row, N - 1);
-    wsrc[i] = W + gr * K + ((lpos ^ swz(row)) << 4);
+    woff[i] = static_cast<uint32_t>(row * K + ((lpos ^ swz(row)) << 4));
   }
-  const uint8_t* asrc[T::kALoads];
+  uint32_t aoff[T::kALoads];
 #pragma unroll
   for (int i = 0; i < T::kALoads; ++i) {
     const int row = (wave * T::kALoads + i) * 8 + lrow8;
-    const int64_t gr = min<int64_t>(m0 + row, M - 1);
-    asrc[i] = A + gr * K + ((lpos ^ swz(row)) << 4);
+    aoff[i] = static_cast<uint32_t>(row * K + ((lpos ^ swz(row)) << 4));
   }
+  const int64_t wrows = min<int64_t>(BN, N - n0), arows = min<int64_t>(BM, M - m0);
+  const uint8_t* wtile = W + n0 * K;
+  const uint8_t* atile = A + m0 * K;
+  const float* stile = sa + m0 * KB;
   // scale slot s = wave*64 + lane (first kSWaves waves) holds the scale of
   // row wq*TM + 16*j + l16, where s = wq*TM + l16*NJ + j
   const bool loads_scales = wave < T::kSWaves;
-  const float* ssrc;
+  uint32_t soff;
   {
     const int s = wave * 64 + lane;
     const int wq = s / T::TM, rem = s % T::TM;
     const int row = wq * T::TM + 16 * (rem % NJ) + rem / NJ;
-    ssrc = sa + min<int64_t>(m0 + row, M - 1) * KB;
+    soff = static_cast<uint32_t>(row * KB * 4);
   }
   // wave-uniform: the weight-scale row address stays in scalar registers
   const int64_t nb = min<int64_t>((n0 + wn * T::TN) / 128, N / 128 - 1);
   const float* swrow = sw + nb * KB;
 
   const uint32_t lds0 = lds_addr(lds);
-  auto issue = [&](int kb) {
+  // Copy p of this wave's part of block kb (p < kPer: W copies, then A
+  // copies; the scale copy goes with p == 0). Inside the K loop the copies
+  // of the block being prefetched are spread over the first MFMA rows.
+  // Each buffer starts at column 128*kb of the tile's first row.
+  auto issue_part = [&](int kb, int p) {
     const uint32_t st = lds0 + (kb % STAGES) * T::kStageBytes;
+    const uint32_t cb = static_cast<uint32_t>(kb) * kBK;
+    if (p < T::kWLoads) {
+      copy16_buf_to_lds(woff[p], make_rsrc(wtile + cb, static_cast<uint32_t>(wrows * K) - cb),
+                        st + (wave * T::kWLoads + p) * 1024);
+    } else {
+      const int q = p - T::kWLoads;
+      copy16_buf_to_lds(aoff[q], make_rsrc(atile + cb, static_cast<uint32_t>(arows * K) - cb),
+                        st + T::kWBytes + (wave * T::kALoads + q) * 1024);
+    }
+    if (p == 0 && loads_scales)
+      copy4_buf_to_lds(soff, make_rsrc(stile + kb, static_cast<uint32_t>(arows * KB * 4) - 4u * kb),
+                       st + T::kWBytes + T::kABytes + wave * 256);
+  };
+  auto issue = [&](int kb) {
 #pragma unroll
-    for (int i = 0; i < T::kWLoads; ++i)
-      copy16_to_lds(wsrc[i] + static_cast<int64_t>(kb) * kBK, st + (wave * T::kWLoads + i) * 1024);
-#pragma unroll
-    for (int i = 0; i < T::kALoads; ++i)
-      copy16_to_lds(asrc[i] + static_cast<int64_t>(kb) * kBK,
-                    st + T::kWBytes + (wave * T::kALoads + i) * 1024);
-    if (loads_scales) copy4_to_lds(ssrc + kb, st + T::kWBytes + T::kABytes + wave * 256);
+    for (int p = 0; p < T::kWLoads + T::kALoads; ++p) issue_part(kb, p);
   };
 
   v4f acc[NI][NJ];
@@ -237,10 +264,38 @@ void gemm_blockscaled_tiled_kernel(
   // before the first fragment read: scalar loads complete out of order, so
   // while one is in flight every wait for an LDS read is a full wait.
   float swb = swrow[0];
-  for (int kb = 0; kb < KB; ++kb) {
+  // Software pipeline across blocks. The MFMAs of the last W row of block
+  // kb-1 are issued after the barrier that opens block kb, interleaved with
+  // the reads of block kb's A fragments (each read refills the registers the
+  // MFMA before it has consumed), so the matrix unit has work while those
+  // first reads are in flight. The scale FMAs of every MFMA row run after the
+  // next row's MFMAs. Before the first block all of this state is zero, which
+  // makes the extra MFMAs and FMAs of the first prologue exact no-ops.
+  v8i af[NJ];
+  v8i wlast;
+  v4f pp[NJ];
+  float csl[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    af[j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    pp[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    csl[j] = 0.0f;
+  }
+  wlast = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  // copies of the prefetched block: kPerRow per MFMA row, rows 0..kDmaRows-1
+  constexpr int kDmaRows = FP8BS_DMA_ROWS < NI - 1 ? FP8BS_DMA_ROWS : NI - 1;
+  constexpr int kPerRow = (kPer + kDmaRows - 1) / kDmaRows;
+  static_assert((kPer + kPerRow - 1) / kPerRow <= NI - 1, "every copy must be issued");
+
+  // One K block. PF: the block STAGES-1 ahead is copied in during this one
+  // (all but the last STAGES-1 blocks); the two loops keep that decision out
+  // of the loop body.
+  auto step = [&](int kb, auto pf) {
+    constexpr bool PF = decltype(pf)::value;
     // this wave's copies of block kb are done once at most the groups of the
-    // blocks issued after it (STAGES-2 of them, fewer near the end) remain
-    const int ahead = min(KB - 1 - kb, STAGES - 2);
+    // blocks issued after it remain: STAGES-2 of them while blocks are being
+    // prefetched, fewer in the last iterations
+    const int ahead = PF ? STAGES - 2 : min(KB - 1 - kb, STAGES - 2);
     if (ahead <= 0) {
       wait_vmcnt<0>();
     } else if (ahead == 1) {
@@ -250,21 +305,19 @@ void gemm_blockscaled_tiled_kernel(
       if (loads_scales) wait_vmcnt<2 * (kPer + 1)>();
       else wait_vmcnt<2 * kPer>();
     }
+    // The last W fragment of block kb-1 (wlast) was read but not yet used:
+    // wait for every LDS read (and the scalar load of the weight scale) so
+    // that no read of block kb-1's stage is in flight past the barrier.
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     // Plain barrier, no memory fence: every wave's part of block kb is in
-    // LDS, and every wave's LDS reads of block kb-1 are complete (they fed
-    // MFMAs already issued), so that stage may be refilled.
+    // LDS, and every wave's LDS reads of block kb-1 have returned, so that
+    // stage may be refilled.
     __builtin_amdgcn_s_barrier();
-    if (kb + STAGES - 1 < KB) issue(kb + STAGES - 1);
     asm volatile("" ::"s"(swb));
     __builtin_amdgcn_sched_barrier(0);
 
     const uint8_t* st = lds + (kb % STAGES) * T::kStageBytes;
     const uint8_t* sA = st + T::kWBytes;
-    // Block prologue in the order the MFMAs need it: the activation scales,
-    // W row 0 and A column 0 first (the first MFMA waits only for those),
-    // the other fragments behind it.
-    v4f pp[NJ], pc[NJ];
-    v8i af[NJ];
     const float* sv = reinterpret_cast<const float*>(st + T::kWBytes + T::kABytes) + wm * T::TM + (lane & 15) * NJ;
     float sav[NJ];
     if constexpr (NJ == 4) {
@@ -275,24 +328,46 @@ void gemm_blockscaled_tiled_kernel(
       sav[0] = v.x; sav[1] = v.y;
     }
     v8i wcur = lds_frag(st, wrow, c0);
-    af[0] = lds_frag(sA, arow, c0);
-    __builtin_amdgcn_sched_barrier(0);
+    // last row of block kb-1; each A fragment is refilled right after its MFMA
+    v4f pc[NJ];
 #pragma unroll
-    for (int j = 1; j < NJ; ++j) af[j] = lds_frag(sA, arow + j * 16, c0);
+    for (int j = 0; j < NJ; ++j) {
+      pc[j] = mfma_16x16x128_fp8(wlast, af[j]);
+      af[j] = lds_frag(sA, arow + j * 16, c0);
+    }
     v8i wnext = lds_frag(st, wrow + 16, c0);
 #pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[NI - 2][j][r] = __builtin_fmaf(pp[j][r], csl[j], acc[NI - 2][j][r]);
+    // row 0 of block kb
+#pragma unroll
     for (int j = 0; j < NJ; ++j) pp[j] = mfma_16x16x128_fp8(wcur, af[j]);
+    if constexpr (PF) {
+#pragma unroll
+      for (int p = 0; p < kPerRow; ++p)
+        if (p < kPer) issue_part(kb + STAGES - 1, p);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[NI - 1][j][r] = __builtin_fmaf(pc[j][r], csl[j], acc[NI - 1][j][r]);
     float cs[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) cs[j] = sav[j] * swb;
-    // W fragments double-buffered: the fragment of row i+1 is read before
-    // the MFMAs of row i, so its LDS latency hides behind NJ MFMAs
+    // rows 1..NI-2; W fragments double-buffered: the fragment of row i+1 is
+    // read before the MFMAs of row i, so its LDS latency hides behind them
 #pragma unroll
-    for (int i = 1; i < NI; ++i) {
+    for (int i = 1; i < NI - 1; ++i) {
       wcur = wnext;
-      if (i + 1 < NI) wnext = lds_frag(st, wrow + (i + 1) * 16, c0);
+      wnext = lds_frag(st, wrow + (i + 1) * 16, c0);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) pc[j] = mfma_16x16x128_fp8(wcur, af[j]);
+      if constexpr (PF) {
+#pragma unroll
+        for (int p = i * kPerRow; p < (i + 1) * kPerRow; ++p)
+          if (p < kPer) issue_part(kb + STAGES - 1, p);
+      }
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -300,26 +375,28 @@ void gemm_blockscaled_tiled_kernel(
 #pragma unroll
       for (int j = 0; j < NJ; ++j) pp[j] = pc[j];
     }
+    // pp holds row NI-2; the last row's fragment waits in wlast
+    wlast = wnext;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) csl[j] = cs[j];
+    __builtin_amdgcn_sched_barrier(0);
+    swb = swrow[min(kb + 1, KB - 1)];
+  };
+  const int kb_pf = max(KB - (STAGES - 1), 0);
+  for (int kb = 0; kb < kb_pf; ++kb) step(kb, std::true_type{});
+  for (int kb = kb_pf; kb < KB; ++kb) step(kb, std::false_type{});
+  {
+    // last row of the last block
+    v4f pc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) pc[j] = mfma_16x16x128_fp8(wlast, af[j]);
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[NI - 1][j][r] = __builtin_fmaf(pp[j][r], cs[j], acc[NI - 1][j][r]);
-    __builtin_amdgcn_sched_barrier(0);
-    swb = swrow[min(kb + 1, KB - 1)];
-#ifdef FP8BS_SCHED_HINT
-    // order: A fragments, scales, W rows 0 and 1 first; then per MFMA row i
-    // the next W fragment (2 reads) and NJ x (1 MFMA + 4 VALU)
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NJ + 1 + 4, 0);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      if (i >= 1 && i + 1 < NI) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      for (int r = 0; r < 4; ++r) {
+        acc[NI - 2][j][r] = __builtin_fmaf(pp[j][r], csl[j], acc[NI - 2][j][r]);
+        acc[NI - 1][j][r] = __builtin_fmaf(pc[j][r], csl[j], acc[NI - 1][j][r]);
       }
-    }
-#endif
   }
 
   // Epilogue through LDS, so that every global store writes whole rows of C.
@@ -355,204 +432,6 @@ void gemm_blockscaled_tiled_kernel(
     const int64_t m = m0 + ml, n = n0 + c * 8;
     if (m < M && n < N) *reinterpret_cast<uint4*>(C + m * N + n) = v;
   }
-}
-
-// ---------------------------------------------------------------------------
-// Register-prefetched variant (one wave per SIMD, three LDS stages): the
-// fragments and scales of K block kb+1 are read from LDS while the MFMAs of
-// block kb run, into a second register set, so no MFMA waits for LDS. The
-// barrier that opens iteration kb makes block kb+1 visible; block kb+3 is
-// then copied into the stage block kb left (its fragments are in registers).
-// ---------------------------------------------------------------------------
-template <int NI, int NJ>
-struct Frags {
-  v8i a[NJ];
-  v8i w[NI];
-  float cs[NJ];
-};
-
-template <int BN, int BM, int WN, int WM>
-__global__ __launch_bounds__(64 * WN * WM) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_blockscaled_rp_kernel(
-    const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
-    const float* __restrict__ sw, uint16_t* __restrict__ C, int64_t M, int64_t N, int64_t K,
-    int tiles_m, int tiles_n) {
-  constexpr int STAGES = 3;
-  using T = TileCfg<BN, BM, WN, WM, STAGES>;
-  constexpr int NI = T::NI, NJ = T::NJ;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * T::kStageBytes];
-
-  const int ntiles = tiles_m * tiles_n;
-  const int per_xcd = (ntiles + 7) / 8;
-  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (t >= ntiles) return;
-  const int group = t / (kGroupM * tiles_n);
-  const int first_m = group * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
-  const int tm = first_m + (t % (kGroupM * tiles_n)) % gsize;
-  const int tn = (t % (kGroupM * tiles_n)) / gsize;
-  const int64_t n0 = static_cast<int64_t>(tn) * BN;
-  const int64_t m0 = static_cast<int64_t>(tm) * BM;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wn = wave % WN;
-  const int wm = wave / WN;
-  const int KB = static_cast<int>(K / kBK);
-
-  const int lrow8 = lane >> 3;
-  const int lpos = lane & 7;
-  const uint8_t* wsrc[T::kWLoads];
-#pragma unroll
-  for (int i = 0; i < T::kWLoads; ++i) {
-    const int row = (wave * T::kWLoads + i) * 8 + lrow8;
-    const int64_t gr = min<int64_t>(n0 + row, N - 1);
-    wsrc[i] = W + gr * K + ((lpos ^ swz(row)) << 4);
-  }
-  const uint8_t* asrc[T::kALoads];
-#pragma unroll
-  for (int i = 0; i < T::kALoads; ++i) {
-    const int row = (wave * T::kALoads + i) * 8 + lrow8;
-    const int64_t gr = min<int64_t>(m0 + row, M - 1);
-    asrc[i] = A + gr * K + ((lpos ^ swz(row)) << 4);
-  }
-  const bool loads_scales = wave < T::kSWaves;
-  const float* ssrc;
-  {
-    const int s = wave * 64 + lane;
-    const int wq = s / T::TM, rem = s % T::TM;
-    const int row = wq * T::TM + 16 * (rem % NJ) + rem / NJ;
-    ssrc = sa + min<int64_t>(m0 + row, M - 1) * KB;
-  }
-  const int64_t nb = min<int64_t>((n0 + wn * T::TN) / 128, N / 128 - 1);
-  const float* swrow = sw + nb * KB;
-
-  const uint32_t lds0 = lds_addr(lds);
-  auto issue = [&](int kb) {
-    const uint32_t st = lds0 + (kb % STAGES) * T::kStageBytes;
-#pragma unroll
-    for (int i = 0; i < T::kWLoads; ++i)
-      copy16_to_lds(wsrc[i] + static_cast<int64_t>(kb) * kBK, st + (wave * T::kWLoads + i) * 1024);
-#pragma unroll
-    for (int i = 0; i < T::kALoads; ++i)
-      copy16_to_lds(asrc[i] + static_cast<int64_t>(kb) * kBK,
-                    st + T::kWBytes + (wave * T::kALoads + i) * 1024);
-    if (loads_scales) copy4_to_lds(ssrc + kb, st + T::kWBytes + T::kABytes + wave * 256);
-  };
-  constexpr int kPer = T::kWLoads + T::kALoads;
-  // wait until this wave's copies of the block issued `behind` groups ago
-  // have landed (`behind` groups issued after it may remain)
-  auto wait_groups = [&](int behind) {
-    if (behind <= 0) wait_vmcnt<0>();
-    else if (loads_scales) wait_vmcnt<kPer + 1>();
-    else wait_vmcnt<kPer>();
-  };
-
-  const int c0 = 2 * (lane >> 4);
-  const int arow = wm * T::TM + (lane & 15);
-  const int wrow = wn * T::TN + (lane & 15);
-  auto read_frags = [&](Frags<NI, NJ>& f, int kb) {
-    const uint8_t* st = lds + (kb % STAGES) * T::kStageBytes;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) f.a[j] = lds_frag(st + T::kWBytes, arow + j * 16, c0);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) f.w[i] = lds_frag(st, wrow + i * 16, c0);
-    const float* sv = reinterpret_cast<const float*>(st + T::kWBytes + T::kABytes) + wm * T::TM + (lane & 15) * NJ;
-    const float swb = swrow[kb];
-    if constexpr (NJ == 4) {
-      const float4 v = *reinterpret_cast<const float4*>(sv);
-      f.cs[0] = v.x * swb; f.cs[1] = v.y * swb; f.cs[2] = v.z * swb; f.cs[3] = v.w * swb;
-    } else {
-      const float2 v = *reinterpret_cast<const float2*>(sv);
-      f.cs[0] = v.x * swb; f.cs[1] = v.y * swb;
-    }
-  };
-
-  v4f acc[NI][NJ];
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  auto compute = [&](const Frags<NI, NJ>& f) {
-    v4f pp[NJ], pc[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) pp[j] = mfma_16x16x128_fp8(f.w[0], f.a[j]);
-#pragma unroll
-    for (int i = 1; i < NI; ++i) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) pc[j] = mfma_16x16x128_fp8(f.w[i], f.a[j]);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i - 1][j][r] = __builtin_fmaf(pp[j][r], f.cs[j], acc[i - 1][j][r]);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) pp[j] = pc[j];
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[NI - 1][j][r] = __builtin_fmaf(pp[j][r], f.cs[j], acc[NI - 1][j][r]);
-  };
-
-  // one iteration: open block kb+1 (wait, barrier), refill the stage block kb
-  // left with block kb+3, read block kb+1 into `nxt`, compute block kb
-  // an iteration with a next block (kb + 1 < KB)
-  auto step = [&](int kb, const Frags<NI, NJ>& cur, Frags<NI, NJ>& nxt) {
-    wait_groups(kb + 2 < KB ? 1 : 0);
-    __builtin_amdgcn_s_barrier();
-    if (kb + 3 < KB) issue(kb + 3);
-    read_frags(nxt, kb + 1);
-    compute(cur);
-    interleave_mfma_ds_valu<NI * NJ, 2 * (NI + NJ) + 1>();
-  };
-
-  Frags<NI, NJ> f0, f1;
-  issue(0);
-  if (KB > 1) issue(1);
-  wait_groups(KB > 1 ? 1 : 0);
-  __builtin_amdgcn_s_barrier();
-  if (KB > 2) issue(2);
-  read_frags(f0, 0);
-  int kb = 0;
-  for (; kb + 2 < KB; kb += 2) {
-    step(kb, f0, f1);
-    step(kb + 1, f1, f0);
-  }
-  if (kb + 1 < KB) {          // two blocks left: kb (in f0) and kb + 1
-    step(kb, f0, f1);
-    compute(f1);
-  } else {                    // one block left: kb (in f0)
-    compute(f0);
-  }
-
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int64_t m = m0 + wm * T::TM + j * 16 + (lane & 15);
-    if (m >= M) continue;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int64_t n = n0 + wn * T::TN + i * 16 + (lane >> 4) * 4;
-      if (n >= N) continue;
-      uint2 o;
-      o.x = bf16x2_rne(acc[i][j][0], acc[i][j][1]);
-      o.y = bf16x2_rne(acc[i][j][2], acc[i][j][3]);
-      *reinterpret_cast<uint2*>(C + m * N + n) = o;
-    }
-  }
-}
-
-template <int BN, int BM, int WN, int WM>
-int launch_rp(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c,
-              int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  const int64_t tiles_m = (M + BM - 1) / BM;
-  const int64_t tiles_n = (N + BN - 1) / BN;
-  const int64_t grid = (tiles_m * tiles_n + 7) / 8 * 8;
-  if (grid > 0x7FFFFFF0LL) return FP8BS_ERR_SHAPE;
-  hipLaunchKernelGGL((gemm_blockscaled_rp_kernel<BN, BM, WN, WM>), dim3(static_cast<unsigned>(grid)),
-                     dim3(64 * WN * WM), 0, st, a, sa, w, sw, c, M, N, K, static_cast<int>(tiles_m),
-                     static_cast<int>(tiles_n));
-  return FP8BS_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -780,7 +659,7 @@ int fp8_gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w
   if (!a_e4m3 || !a_scale || !w_e4m3 || !w_scale || !c_bf16) return FP8BS_ERR_NULL;
   if (M < 1 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
   if (M > (INT64_MAX / K) || M > (INT64_MAX / N) || N > (INT64_MAX / K)) return FP8BS_ERR_SHAPE;
-  if (K / 128 > 0x7FFFFFFF || (M + 127) / 128 > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  if (K > (int64_t{1} << 22) || (M + 127) / 128 > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
   if (use_decode(M) && K / 128 > static_cast<int64_t>(kDecMaxSplits) * kDecMaxKb) return FP8BS_ERR_SHAPE;
   if (!aligned(a_e4m3, 16) || !aligned(w_e4m3, 16) || !aligned(c_bf16, 16) ||
       !aligned(a_scale, 4) || !aligned(w_scale, 4))
@@ -814,8 +693,6 @@ int fp8_gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w
   rc = launch_tiled<256, 256, 2, 4, 2, 2>(a, a_scale, w, w_scale, c, M, N, K, st);
 #elif FP8BS_GEMM_TILE == 3
   rc = launch_tiled<256, 128, 2, 2, 3, 1>(a, a_scale, w, w_scale, c, M, N, K, st);
-#elif FP8BS_GEMM_TILE == 4
-  rc = launch_rp<256, 128, 2, 2>(a, a_scale, w, w_scale, c, M, N, K, st);
 #endif
   if (rc != FP8BS_OK) return rc;
   return launch_status();

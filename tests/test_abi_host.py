@@ -80,6 +80,8 @@ def test_gemm_argument_errors(L):
     assert f(P, P, P, P, P, 4, 100, 128, None, 0, None) == ESHAPE
     assert f(P, P, P, P, P, 4, 128, 64, None, 0, None) == ESHAPE
     assert f(P, P, P, P, P, 4, 128, 130, None, 0, None) == ESHAPE
+    # K above 2^22 (tile-relative copy offsets are 32-bit), tiled path (M > 64)
+    assert f(P, P, P, P, P, 256, 128, (1 << 22) + 128, None, 0, None) == ESHAPE
     assert f(PU, P, P, P, P, 4, 128, 128, None, 0, None) == EALIGN
     assert f(P, P, P, P, PU, 4, 128, 128, None, 0, None) == EALIGN
     assert f(P, P + 1, P, P, P, 4, 128, 128, None, 0, None) == EALIGN
