@@ -13,9 +13,9 @@ N=2048, K=7168), c2 per-tensor sweep (K=2048), c1 tiny (32x512x512).
 
 Prints ONE JSON line. ``value`` is the step throughput expressed as GEMM
 TFLOP/s (2*M*N*K per step / step time; per-tensor-only workloads use GB/s).
-The per-stage times come from HIP events recorded around each launch inside
-the timed region on the launch stream; ``roofline`` is for the dominant
-kernel. ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+The per-stage times come from HIP events around back-to-back launches of
+each stage alone on the launch stream (replayed from a graph of their own
+under --graph); ``roofline`` is for the dominant kernel. ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
 workload on the host cores.
 """
 from __future__ import annotations
@@ -205,10 +205,26 @@ def time_steps(torch, wl, steps, warmup, graph):
 
     per_stage = []
     for _, fn, _, _ in wl.stages:
+        gs = None
+        if graph:
+            # the stage's launches alone, replayed from a graph of their own
+            gs = torch.cuda.CUDAGraph()
+            cs = torch.cuda.Stream()
+            cs.wait_stream(st)
+            with torch.cuda.stream(cs):
+                with torch.cuda.graph(gs, stream=cs):
+                    for i in range(steps):
+                        fn(i)
+            torch.cuda.synchronize()
+            gs.replay()
+            torch.cuda.synchronize()
         a, b = ev(), ev()
         a.record(st)
-        for i in range(steps):
-            fn(i)
+        if gs is not None:
+            gs.replay()
+        else:
+            for i in range(steps):
+                fn(i)
         b.record(st)
         torch.cuda.synchronize()
         per_stage.append(a.elapsed_time(b) / steps)
@@ -334,7 +350,8 @@ def main():
                 f"{max(1, args.rotate)} rotated copies)",
         "config": wl.config,
         "timing": ("step: HIP events around all steps" + (" (HIP graph replay)" if args.graph else "")
-                   + "; stages: HIP events around back-to-back launches of each stage"),
+                   + "; stages: HIP events around back-to-back launches of each stage"
+                   + (" (each stage replayed from a graph of its own)" if args.graph else "")),
         "stages": stages,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -435,8 +435,132 @@ void gemm_blockscaled_tiled_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernel (M <= 64): the GEMM is bound by streaming W from HBM, so the
-// work is cut into many pieces of W: workgroup (n tile of 64 rows, K split)
+// Decode kernels. At decode shapes the GEMM is bound by streaming W from HBM.
+//
+// Small M (M <= 16): workgroup = 16 W rows (one MFMA tile of n) over the
+// whole of K, eight
+// waves; wave w takes K blocks w, w+8, w+16, ... and keeps kDecDepth of them
+// in flight, W fragments and A fragments loaded straight from global memory
+// into registers (A is small and stays in L2). Each K block is one MFMA per
+// 16 activation rows plus the scale FMAs. The eight partial sums are added
+// through LDS in wave order, so the result is deterministic and no second
+// kernel or workspace is needed. Every workgroup reads all of A (through
+// L2), which costs little while A is at most 16 rows.
+// ---------------------------------------------------------------------------
+constexpr int kDecWaves = 8;
+constexpr int kDecStreamMaxM = 16;
+
+// MT: 16-row groups of A (M <= 16*MT); kDecDepth: K blocks in flight per wave
+template <int MT, int kDecDepth>
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_blockscaled_decode_stream_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
+    const float* __restrict__ sw, uint16_t* __restrict__ C, int M, int64_t N, int64_t K) {
+  __shared__ float4 red[kDecWaves][MT][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int KB = static_cast<int>(K / kBK);
+
+  // lane l supplies W row n0 + l%16 and A rows 16j + l%16 (rows past M read
+  // row M-1: valid memory, results never stored), K bytes 32*(l/16) ..+32
+  const int koff = 32 * (lane >> 4);
+  const uint8_t* wp = W + (n0 + (lane & 15)) * K + koff;
+  const uint8_t* ap[MT];
+  const float* sp[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    const int64_t m = min(j * 16 + (lane & 15), M - 1);
+    ap[j] = A + m * K + koff;
+    sp[j] = sa + m * KB;
+  }
+  const float* swrow = sw + (n0 / 128) * KB;
+
+  // this wave's K blocks: kb = wave + kDecWaves * t, t = 0 .. nt-1
+  const int nt = KB > wave ? (KB - wave + kDecWaves - 1) / kDecWaves : 0;
+  uint4 wq[kDecDepth][2];
+  uint4 aq[kDecDepth][MT][2];
+  float sq[kDecDepth][MT];
+  auto load = [&](int d, int t) {
+    const int64_t kb = wave + static_cast<int64_t>(kDecWaves) * t;
+    wq[d][0] = *reinterpret_cast<const uint4*>(wp + kb * kBK);
+    wq[d][1] = *reinterpret_cast<const uint4*>(wp + kb * kBK + 16);
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      aq[d][j][0] = *reinterpret_cast<const uint4*>(ap[j] + kb * kBK);
+      aq[d][j][1] = *reinterpret_cast<const uint4*>(ap[j] + kb * kBK + 16);
+      sq[d][j] = sp[j][kb];
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < kDecDepth; ++d)
+    if (d < nt) load(d, d);
+
+  v4f acc[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t0 = 0; t0 < nt; t0 += kDecDepth) {
+#pragma unroll
+    for (int d = 0; d < kDecDepth; ++d) {
+      const int t = t0 + d;
+      if (t < nt) {
+        const v8i wf = v8i{(int)wq[d][0].x, (int)wq[d][0].y, (int)wq[d][0].z, (int)wq[d][0].w,
+                           (int)wq[d][1].x, (int)wq[d][1].y, (int)wq[d][1].z, (int)wq[d][1].w};
+        v8i af[MT];
+        float cs[MT];
+        const float swb = swrow[wave + kDecWaves * t];
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+          af[j] = v8i{(int)aq[d][j][0].x, (int)aq[d][j][0].y, (int)aq[d][j][0].z, (int)aq[d][j][0].w,
+                      (int)aq[d][j][1].x, (int)aq[d][j][1].y, (int)aq[d][j][1].z, (int)aq[d][j][1].w};
+          cs[j] = sq[d][j] * swb;
+        }
+        if (t + kDecDepth < nt) load(d, t + kDecDepth);
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+          const v4f p = mfma_16x16x128_fp8(wf, af[j]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(p[r], cs[j], acc[j][r]);
+        }
+      }
+    }
+  }
+
+  // lane holds D[n = n0 + 4*(lane/16) + r][m = 16j + lane%16]; add the
+  // waves' partial sums in wave order
+#pragma unroll
+  for (int j = 0; j < MT; ++j) red[wave][j][lane] = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < MT * 64) {
+    const int j = t / 64, l = t % 64;
+    const int m = j * 16 + (l & 15);
+    if (m < M) {
+      float4 s = red[0][j][l];
+#pragma unroll
+      for (int w = 1; w < kDecWaves; ++w) {
+        const float4 v = red[w][j][l];
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+      }
+      const int64_t n = n0 + 4 * (l >> 4);
+      uint2 o;
+      o.x = bf16x2_rne(s.x, s.y);
+      o.y = bf16x2_rne(s.z, s.w);
+      *reinterpret_cast<uint2*>(C + m * N + n) = o;
+    }
+  }
+}
+
+int launch_decode_stream(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c,
+                         int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_blockscaled_decode_stream_kernel<1, 4>), dim3(static_cast<unsigned>(N / 16)),
+                     dim3(64 * kDecWaves), 0, st, a, sa, w, sw, c, static_cast<int>(M), N, K);
+  return FP8BS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Larger decode M (16 < M <= 64): the work is cut into many pieces of W so
+// that A is shared: workgroup (n tile of 64 rows, K split)
 // has four waves, wave w owning W rows 16w..16w+15 of the tile. Each wave
 // loads its W fragments straight from global memory into registers
 // (kDepth K blocks in flight), the K split's slice of A (at most 64 rows) is
@@ -467,6 +591,23 @@ __global__ __launch_bounds__(256) void gemm_blockscaled_decode_kernel(
   const int nkb = min(KB - kb0, kb_per);
   if (nkb <= 0) return;
 
+  const int64_t nrow = n0 + wave * 16 + (lane & 15);          // this lane's W row
+  const uint8_t* wp = W + min<int64_t>(nrow, N - 1) * K + static_cast<int64_t>(kb0) * kBK + 32 * (lane >> 4);
+  const float* swrow = sw + ((n0 + wave * 16) / 128) * KB + kb0;
+  int mrow[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) mrow[j] = min(j * 16 + (lane & 15), M - 1);
+
+  // W fragments first: their HBM latency overlaps the staging of A
+  uint4 wq[kDecDepth][2];
+#pragma unroll
+  for (int d = 0; d < kDecDepth; ++d) {
+    if (d < nkb) {
+      wq[d][0] = *reinterpret_cast<const uint4*>(wp + d * kBK);
+      wq[d][1] = *reinterpret_cast<const uint4*>(wp + d * kBK + 16);
+    }
+  }
+
   // stage A rows [0, 16*MT) x K blocks [kb0, kb0 + nkb) in LDS (rows >= M
   // read row M-1: valid memory, results never stored), swizzled as in the
   // tiled kernel
@@ -480,21 +621,6 @@ __global__ __launch_bounds__(256) void gemm_blockscaled_decode_kernel(
     *reinterpret_cast<uint4*>(lds + (kk * MP + row) * 128 + ((c ^ swz(row)) << 4)) = v;
   }
 
-  const int64_t nrow = n0 + wave * 16 + (lane & 15);          // this lane's W row
-  const uint8_t* wp = W + min<int64_t>(nrow, N - 1) * K + static_cast<int64_t>(kb0) * kBK + 32 * (lane >> 4);
-  const float* swrow = sw + ((n0 + wave * 16) / 128) * KB + kb0;
-  int mrow[MT];
-#pragma unroll
-  for (int j = 0; j < MT; ++j) mrow[j] = min(j * 16 + (lane & 15), M - 1);
-
-  uint4 wq[kDecDepth][2];
-#pragma unroll
-  for (int d = 0; d < kDecDepth; ++d) {
-    if (d < nkb) {
-      wq[d][0] = *reinterpret_cast<const uint4*>(wp + d * kBK);
-      wq[d][1] = *reinterpret_cast<const uint4*>(wp + d * kBK + 16);
-    }
-  }
   __syncthreads();
 
   v4f acc[MT];
@@ -650,7 +776,7 @@ extern "C" {
 
 size_t fp8_gemm_blockscaled_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return 0;
-  return use_decode(M) ? decode_workspace_bytes(M, N, K) : 0;
+  return use_decode(M) && M > kDecStreamMaxM ? decode_workspace_bytes(M, N, K) : 0;
 }
 
 int fp8_gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m3,
@@ -660,7 +786,8 @@ int fp8_gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w
   if (M < 1 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
   if (M > (INT64_MAX / K) || M > (INT64_MAX / N) || N > (INT64_MAX / K)) return FP8BS_ERR_SHAPE;
   if (K > (int64_t{1} << 22) || (M + 127) / 128 > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
-  if (use_decode(M) && K / 128 > static_cast<int64_t>(kDecMaxSplits) * kDecMaxKb) return FP8BS_ERR_SHAPE;
+  if (use_decode(M) && M > kDecStreamMaxM && K / 128 > static_cast<int64_t>(kDecMaxSplits) * kDecMaxKb)
+    return FP8BS_ERR_SHAPE;
   if (!aligned(a_e4m3, 16) || !aligned(w_e4m3, 16) || !aligned(c_bf16, 16) ||
       !aligned(a_scale, 4) || !aligned(w_scale, 4))
     return FP8BS_ERR_ALIGN;
@@ -675,7 +802,10 @@ int fp8_gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w
   (void)hipGetLastError();
   int rc;
   if (use_decode(M)) {
-    rc = launch_decode(a, a_scale, w, w_scale, c, static_cast<float*>(workspace), M, N, K, st);
+    if (M <= kDecStreamMaxM)
+      rc = launch_decode_stream(a, a_scale, w, w_scale, c, M, N, K, st);
+    else
+      rc = launch_decode(a, a_scale, w, w_scale, c, static_cast<float*>(workspace), M, N, K, st);
     if (rc != FP8BS_OK) return rc;
     return launch_status();
   }

@@ -105,10 +105,12 @@ int fp8_amax_quant_tensor(const void* x_bf16, int64_t numel,
  *   w_scale  [N/128, K/128] fp32, 4-byte aligned    (input)
  *   c_bf16   [M, N] bf16, 16-byte aligned           (output, RNE from fp32)
  *   workspace  at least fp8_gemm_blockscaled_workspace_bytes(M, N, K) bytes,
- *              16-byte aligned (NULL allowed when that size is 0)
+ *              16-byte aligned (NULL allowed when that size is 0, which is
+ *              the case unless 16 < M <= 64); contents on entry do not
+ *              matter; not to be shared by calls that can run concurrently
  * Requires M >= 1, N >= 128, K >= 128, N % 128 == 0, K % 128 == 0,
  * K <= 4194304 (32-bit offsets within a 256-row tile), and K <= 65536 when
- * M <= 64 (the decode path splits K into at most 32 parts).
+ * 16 < M <= 64 (that path splits K into at most 32 parts).
  * Results agree with the exact product of the dequantized operands within
  * fp32 accumulation error; the order of the fp32 operations is the
  * library's own, so results are deterministic but not bit-equal to another

@@ -117,6 +117,10 @@ def test_python_binding_rejects_bad_tensors():
         fb.fp8_act_quant_block(torch.zeros((4, 128), dtype=torch.float32))
 
 
-def test_gemm_decode_k_limit(L):
-    # M <= 64 splits K into at most 32 parts of at most 16 blocks
-    assert L.fp8_gemm_blockscaled(P, P, P, P, P, 8, 128, 128 * 513, None, 0, None) == ESHAPE
+def test_gemm_k_limits(L):
+    # copy offsets within a tile are 32-bit: K above 2^22 is rejected
+    assert L.fp8_gemm_blockscaled(P, P, P, P, P, 8, 128, (1 << 22) + 128, None, 0, None) == ESHAPE
+    # 16 < M <= 64 splits K into at most 32 parts of at most 16 blocks
+    assert L.fp8_gemm_blockscaled(P, P, P, P, P, 32, 128, 128 * 513, None, 0, None) == ESHAPE
+    assert L.fp8_gemm_blockscaled_workspace_bytes(8, 2048, 7168) == 0
+    assert L.fp8_gemm_blockscaled_workspace_bytes(32, 2048, 7168) > 0

@@ -195,23 +195,29 @@ def test_bit_exact_against_matrix_core_model(dist):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (5, 256, 1024), (16, 2048, 7168), (17, 384, 2048),
-                                   (33, 640, 4096), (64, 2048, 7168), (64, 128, 128 * 40), (48, 7168, 2048)])
+                                   (33, 640, 4096), (64, 2048, 7168), (64, 128, 128 * 40), (48, 7168, 2048),
+                                   (3, 256, 128 * 7), (16, 128, 128 * 600), (40, 128, 128 * 500)])
 def test_decode_shapes(M, N, K):
-    # M <= 64 runs the W-streaming split-K path: several K splits, fp32
-    # partials in the workspace, reduced in split order
+    # M <= 16: eight waves per 16 W rows, each taking every eighth K block,
+    # partial sums added in wave order (K = 7 blocks leaves a wave without a
+    # block; K = 600 blocks runs many prefetch rounds per wave).
+    # 16 < M <= 64: several K splits, fp32 partials in the workspace, reduced
+    # in split order.
     rng = np.random.default_rng(M * 7 + N + K)
     a = synth.f64_to_bf16_bits(rng.standard_normal((M, K)) * 3)
     w = synth.f64_to_bf16_bits(rng.standard_normal((N, K)) * 0.02)
     check_full(*operands(a, w), f"decode {M}x{N}x{K}")
 
 
-def test_decode_workspace_size_and_reuse():
+def test_gemm_workspace_size_and_reuse():
     fb = binding()
-    M, N, K = 8, 2048, 7168
+    N, K = 2048, 7168
+    for M in (1, 8, 16, 65, 4096):
+        assert fb.fp8_gemm_blockscaled_workspace_bytes(M, N, K) == 0
+    M = 32
     wsb = fb.fp8_gemm_blockscaled_workspace_bytes(M, N, K)
     assert wsb % (M * N * 4) == 0 and wsb >= M * N * 4
-    assert fb.fp8_gemm_blockscaled_workspace_bytes(4096, N, K) == 0
-    d = synth.gen_c3(8)
+    d = synth.gen_c3(M)
     qa, sa, qw, sw = operands(d["a"], d["w"])
     args = (u8_to_dev(qa), f32_to_dev(sa), u8_to_dev(qw), f32_to_dev(sw))
     ws = torch.full((wsb,), 0x7F, dtype=torch.uint8, device="cuda:0")     # garbage on entry
