@@ -107,7 +107,7 @@ class Workload:
             q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
             s = torch.empty((1,), dtype=torch.float32, device=dev)
             wsb = fb.fp8_amax_quant_tensor_workspace_bytes(numel)
-            ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device=dev)
+            ws = torch.zeros((max(wsb, 16),), dtype=torch.uint8, device=dev)
             self.stages.append(("amax_quant_tensor",
                                 lambda i: fb.fp8_amax_quant_tensor(xs[i % rot], out=(q, s), workspace=ws),
                                 3 * numel + 4, 0))
@@ -148,7 +148,7 @@ class Workload:
             qt = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
             st = torch.empty((1,), dtype=torch.float32, device=dev)
             twsb = fb.fp8_amax_quant_tensor_workspace_bytes(M * K)
-            tws = torch.empty((max(twsb, 16),), dtype=torch.uint8, device=dev)
+            tws = torch.zeros((max(twsb, 16),), dtype=torch.uint8, device=dev)
             self.stages.append(("amax_quant_tensor",
                                 lambda i: fb.fp8_amax_quant_tensor(a_s[i % rot], out=(qt, st), workspace=tws),
                                 3 * M * K + 4, 0))

@@ -61,11 +61,21 @@ def test_all_zero_and_tiny(numel):
 
 
 def test_deterministic_and_reusable_workspace():
+    # one workspace, garbage on entry, reused across calls of different sizes
     fb = binding()
+    sizes = (1 << 20, (3 << 20) + 9, 40_000, 1 << 22)
+    wsb = max(fb.fp8_amax_quant_tensor_workspace_bytes(n) for n in sizes)
+    ws = torch.full((wsb,), 255, dtype=torch.uint8, device="cuda:0")
     x = bf16_to_dev(synth.gen_c2(1024)["x"])
-    ws = torch.full((fb.fp8_amax_quant_tensor_workspace_bytes(x.numel()),), 255,
-                    dtype=torch.uint8, device="cuda:0")
     q1, s1 = fb.fp8_amax_quant_tensor(x, workspace=ws)
     q2, s2 = fb.fp8_amax_quant_tensor(x, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(q1.view(torch.uint8), q2.view(torch.uint8)) and torch.equal(s1, s2)
+    rng = np.random.default_rng(5)
+    for n in sizes:
+        bits = synth.f64_to_bf16_bits(rng.standard_normal(n) * 2.0)
+        q, s = fb.fp8_amax_quant_tensor(bf16_to_dev(bits), workspace=ws)
+        torch.cuda.synchronize()
+        q_ref, s_ref = quant.amax_quant_tensor(bits)
+        assert to_f32(s).view(np.uint32)[0] == np.float32(s_ref).view(np.uint32), n
+        assert np.array_equal(to_u8(q), q_ref), n
