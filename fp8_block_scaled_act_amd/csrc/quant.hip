@@ -15,6 +15,13 @@
 #include "device_common.h"
 #include "host_common.h"
 
+#ifndef FP8BS_AQ_BPG
+#define FP8BS_AQ_BPG 1
+#endif
+#ifndef FP8BS_AQ_NT
+#define FP8BS_AQ_NT 0
+#endif
+
 namespace fp8bs {
 namespace {
 
@@ -27,6 +34,12 @@ constexpr int kThreads = 256;
 // block amax is a 3-step DPP max inside the 8-lane group.
 // ---------------------------------------------------------------------------
 
+__device__ __forceinline__ void store_nt2(uint2 v, uint2* p) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+}
+
 // quantize the 8 bf16 of a uint4 with scale s (and r = 1/s on the fast path)
 template <bool kFast>
 __device__ __forceinline__ uint2 quant8(const uint4 v, float s, float r) {
@@ -37,39 +50,60 @@ __device__ __forceinline__ uint2 quant8(const uint4 v, float s, float r) {
   return make_uint2(pack4_e4m3(f[0], f[1], f[2], f[3]), pack4_e4m3(f[4], f[5], f[6], f[7]));
 }
 
+// BPG blocks per 8-lane group (all loads issued first); NT: codes stored
+// non-temporally
+template <int BPG, bool NT>
 __global__ __launch_bounds__(kThreads) void act_quant_block_kernel(
     const uint4* __restrict__ x, uint2* __restrict__ q, float* __restrict__ scale,
     int64_t nblocks) {
-  const int64_t blk = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 3;
+  const int64_t grp = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 3;
   const int sub = threadIdx.x & 7;
-  if (blk >= nblocks) return;  // whole 8-lane groups leave together
+  const int64_t blk0 = grp * BPG;
+  if (blk0 >= nblocks) return;  // whole 8-lane groups leave together
 
-  const uint4 v0 = x[blk * 16 + sub];
-  const uint4 v1 = x[blk * 16 + 8 + sub];
-
-  float m = 0.0f;
-  m = absmax2(v0.x, m); m = absmax2(v0.y, m); m = absmax2(v0.z, m); m = absmax2(v0.w, m);
-  m = absmax2(v1.x, m); m = absmax2(v1.y, m); m = absmax2(v1.z, m); m = absmax2(v1.w, m);
-  const float amax = group8_max(m);
-
-  const float s = div_ieee(amax, kE4m3Max);
-  const bool fast = s >= kFastScaleMin;
-  uint2 o0, o1;
-  if (__builtin_expect(__ballot(!fast) == 0, 1)) {
-    const float r = div_ieee(1.0f, s);
-    o0 = quant8<true>(v0, s, r);
-    o1 = quant8<true>(v1, s, r);
-  } else {
-    o0 = quant8<false>(v0, s, 0.0f);
-    o1 = quant8<false>(v1, s, 0.0f);
+  uint4 v[BPG][2];
+#pragma unroll
+  for (int b = 0; b < BPG; ++b) {
+    const int64_t blk = blk0 + b;
+    if (BPG == 1 || blk < nblocks) {
+      v[b][0] = x[blk * 16 + sub];
+      v[b][1] = x[blk * 16 + 8 + sub];
+    }
   }
-  if (amax == 0.0f) {  // all-zero block: scale 0, codes 0x00
-    o0 = make_uint2(0u, 0u);
-    o1 = make_uint2(0u, 0u);
+#pragma unroll
+  for (int b = 0; b < BPG; ++b) {
+    const int64_t blk = blk0 + b;
+    if (BPG > 1 && blk >= nblocks) break;   // uniform over the group
+    const uint4 v0 = v[b][0], v1 = v[b][1];
+    float m = 0.0f;
+    m = absmax2(v0.x, m); m = absmax2(v0.y, m); m = absmax2(v0.z, m); m = absmax2(v0.w, m);
+    m = absmax2(v1.x, m); m = absmax2(v1.y, m); m = absmax2(v1.z, m); m = absmax2(v1.w, m);
+    const float amax = group8_max(m);
+
+    const float s = div_ieee(amax, kE4m3Max);
+    const bool fast = s >= kFastScaleMin;
+    uint2 o0, o1;
+    if (__builtin_expect(__ballot(!fast) == 0, 1)) {
+      const float r = div_ieee(1.0f, s);
+      o0 = quant8<true>(v0, s, r);
+      o1 = quant8<true>(v1, s, r);
+    } else {
+      o0 = quant8<false>(v0, s, 0.0f);
+      o1 = quant8<false>(v1, s, 0.0f);
+    }
+    if (amax == 0.0f) {  // all-zero block: scale 0, codes 0x00
+      o0 = make_uint2(0u, 0u);
+      o1 = make_uint2(0u, 0u);
+    }
+    if constexpr (NT) {
+      store_nt2(o0, q + blk * 16 + sub);
+      store_nt2(o1, q + blk * 16 + 8 + sub);
+    } else {
+      q[blk * 16 + sub] = o0;
+      q[blk * 16 + 8 + sub] = o1;
+    }
+    if (sub == 0) scale[blk] = s;
   }
-  q[blk * 16 + sub] = o0;
-  q[blk * 16 + 8 + sub] = o1;
-  if (sub == 0) scale[blk] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -348,11 +382,13 @@ int fp8_act_quant_block(const void* x_bf16, int64_t M, int64_t K, void* q_e4m3, 
   const DeviceInfo dev = current_device();
   if (dev.status != FP8BS_OK) return dev.status;
   const int64_t nblocks = M * (K / 128);
-  const int64_t grid = (nblocks * 8 + kThreads - 1) / kThreads;
+  constexpr int kBpg = FP8BS_AQ_BPG;
+  const int64_t groups = (nblocks + kBpg - 1) / kBpg;
+  const int64_t grid = (groups * 8 + kThreads - 1) / kThreads;
   if (grid > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(act_quant_block_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
-                     as_stream(stream), static_cast<const uint4*>(x_bf16),
+  hipLaunchKernelGGL((act_quant_block_kernel<kBpg, FP8BS_AQ_NT != 0>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kThreads), 0, as_stream(stream), static_cast<const uint4*>(x_bf16),
                      static_cast<uint2*>(q_e4m3), scale, nblocks);
   return launch_status();
 }
