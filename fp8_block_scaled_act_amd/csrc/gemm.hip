@@ -438,21 +438,24 @@ void gemm_blockscaled_tiled_kernel(
 // Decode kernels. At decode shapes the GEMM is bound by streaming W from HBM.
 //
 // Small M (M <= 16): workgroup = 16 W rows (one MFMA tile of n) over the
-// whole of K, eight
-// waves; wave w takes K blocks w, w+8, w+16, ... and keeps kDecDepth of them
-// in flight, W fragments and A fragments loaded straight from global memory
+// whole of K, sixteen waves; wave w takes K blocks w, w+16, w+32, ... and
+// keeps kDecDepth of them in flight, W fragments and A fragments loaded
+// straight from global memory
 // into registers (A is small and stays in L2). Each K block is one MFMA per
-// 16 activation rows plus the scale FMAs. The eight partial sums are added
+// 16 activation rows plus the scale FMAs. The sixteen partial sums are added
 // through LDS in wave order, so the result is deterministic and no second
 // kernel or workspace is needed. Every workgroup reads all of A (through
 // L2), which costs little while A is at most 16 rows.
 // ---------------------------------------------------------------------------
-constexpr int kDecWaves = 8;
+#ifndef FP8BS_DEC_WAVES
+#define FP8BS_DEC_WAVES 16
+#endif
+constexpr int kDecWaves = FP8BS_DEC_WAVES;
 constexpr int kDecStreamMaxM = 16;
 
 // MT: 16-row groups of A (M <= 16*MT); kDecDepth: K blocks in flight per wave
 template <int MT, int kDecDepth>
-__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(kDecWaves / 4, kDecWaves / 4)))
 void gemm_blockscaled_decode_stream_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, uint16_t* __restrict__ C, int M, int64_t N, int64_t K) {

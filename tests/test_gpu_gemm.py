@@ -198,9 +198,9 @@ def test_bit_exact_against_matrix_core_model(dist):
                                    (33, 640, 4096), (64, 2048, 7168), (64, 128, 128 * 40), (48, 7168, 2048),
                                    (3, 256, 128 * 7), (16, 128, 128 * 600), (40, 128, 128 * 500)])
 def test_decode_shapes(M, N, K):
-    # M <= 16: eight waves per 16 W rows, each taking every eighth K block,
-    # partial sums added in wave order (K = 7 blocks leaves a wave without a
-    # block; K = 600 blocks runs many prefetch rounds per wave).
+    # M <= 16: sixteen waves per 16 W rows, each taking every sixteenth K
+    # block, partial sums added in wave order (K = 7 blocks leaves waves
+    # without a block; K = 600 blocks runs many prefetch rounds per wave).
     # 16 < M <= 64: several K splits, fp32 partials in the workspace, reduced
     # in split order.
     rng = np.random.default_rng(M * 7 + N + K)
