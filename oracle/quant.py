@@ -24,6 +24,16 @@ The rule for a group G of bf16 values x:
     q[i]  = e4m3(clamp(fl32(x[i] / s), -448, 448)) (fp32 division, then RNE)
 with the reading that a group with amax = 0 gets s = 0 and all-zero (0x00)
 codes, since x / 0 is undefined and every element of such a group is zero.
+
+The power-of-two ("ue8m0") variants (the DeepSeek-V3 page's benchmark of
+``act_quant_kernel`` passes ``scale_fmt="ue8m0"``; the page gives no formula)
+take, as the plainest reading, the smallest power of two not below amax/448,
+so that |x / s| <= 448 still holds and dequantization is exact:
+    s     = 2^e,  e = max(ceil(log2(amax / 448)), -127)   (exact; -127 is the
+            smallest exponent an unsigned e8m0 scale byte holds)
+    q[i]  = e4m3(clamp(fl32(x[i] / s), -448, 448))        (the quotient is exact
+            unless it falls below the fp32 normal range, then correctly rounded)
+and the same amax = 0 reading (s = 0, codes 0x00).
 """
 from __future__ import annotations
 
@@ -50,6 +60,38 @@ def _quant_groups(xf: np.ndarray):
     y = np.clip(y, -F448, F448)
     q = e4m3.encode(y)
     q[zero] = 0                                         # all-zero group
+    return q, s
+
+
+UE8M0_MIN_EXP = -127
+
+
+def ue8m0_scale(amax: np.ndarray) -> np.ndarray:
+    """Smallest power of two s >= amax / 448 (s >= 2^-127); 0 where amax is 0.
+
+    Decided with exact comparisons: amax is a float32 and 448 * 2^e is exact in
+    float64, so ``448 * 2^(e-1) < amax <= 448 * 2^e`` fixes e without rounding.
+    """
+    a = np.asarray(amax, dtype=np.float32).astype(np.float64)
+    pos = a > 0
+    _, E = np.frexp(np.where(pos, a / 448.0, 1.0))      # a/448 in [2^(E-1), 2^E), approximately
+    e = E.astype(np.int64)
+    e = np.where(448.0 * np.ldexp(1.0, e - 1) >= a, e - 1, e)
+    e = np.where(448.0 * np.ldexp(1.0, e) < a, e + 1, e)
+    e = np.maximum(e, UE8M0_MIN_EXP)
+    return np.where(pos, np.ldexp(1.0, e), 0.0).astype(np.float32)
+
+
+def _quant_groups_ue8m0(xf: np.ndarray):
+    """As _quant_groups with the power-of-two scale."""
+    amax = np.max(np.abs(xf), axis=1)
+    s = ue8m0_scale(amax)
+    zero = s == 0
+    safe = np.where(zero, np.float32(1.0), s)
+    y = (xf / safe[:, None]).astype(np.float32)         # IEEE fp32 division
+    y = np.clip(y, -F448, F448)
+    q = e4m3.encode(y)
+    q[zero] = 0
     return q, s
 
 
@@ -97,5 +139,35 @@ def weight_quant_block(w_bits: np.ndarray, block: int = 128):
     nb, kb = N // block, K // block
     wf = bf16_to_f32(w_bits).reshape(nb, block, kb, block).transpose(0, 2, 1, 3)
     q, s = _quant_groups(wf.reshape(nb * kb, block * block))
+    q = q.reshape(nb, kb, block, block).transpose(0, 2, 1, 3).reshape(N, K)
+    return np.ascontiguousarray(q), s.reshape(nb, kb)
+
+
+def act_quant_block_ue8m0(x_bits: np.ndarray, block: int = 128):
+    """1x128 block quantization with power-of-two scales (module docstring).
+
+    Same layout as ``act_quant_block``.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    M, K = x_bits.shape
+    if K % block:
+        raise ValueError("K must be a multiple of the block size")
+    xf = bf16_to_f32(x_bits).reshape(M * (K // block), block)
+    q, s = _quant_groups_ue8m0(xf)
+    return q.reshape(M, K), s.reshape(M, K // block)
+
+
+def weight_quant_block_ue8m0(w_bits: np.ndarray, block: int = 128):
+    """128x128 block quantization with power-of-two scales (module docstring).
+
+    Same layout as ``weight_quant_block``.
+    """
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    N, K = w_bits.shape
+    if N % block or K % block:
+        raise ValueError("N and K must be multiples of the block size")
+    nb, kb = N // block, K // block
+    wf = bf16_to_f32(w_bits).reshape(nb, block, kb, block).transpose(0, 2, 1, 3)
+    q, s = _quant_groups_ue8m0(wf.reshape(nb * kb, block * block))
     q = q.reshape(nb, kb, block, block).transpose(0, 2, 1, 3).reshape(N, K)
     return np.ascontiguousarray(q), s.reshape(nb, kb)

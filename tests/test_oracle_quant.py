@@ -252,3 +252,108 @@ def test_weight_quant_block_rules():
     es, ec = brute_group(list(blk[:1]) + list(blk))   # same max set
     amax = max(abs(bf16_value(b)) for b in blk)
     assert float(s[1, 2]) == float(fl32(amax / 448))
+
+
+# --------------------------------------------------------------------------
+# power-of-two ("ue8m0") scales
+
+def exact_pow2_scale(amax: Fraction) -> Fraction:
+    """Smallest 2^e >= amax/448 with e >= -127, by exact search (0 for amax 0)."""
+    if amax == 0:
+        return Fraction(0)
+    e = -127
+    while Fraction(2) ** e * 448 < amax:
+        e += 1
+    return Fraction(2) ** e
+
+
+def test_ue8m0_scale_exhaustive_over_bf16():
+    # every positive finite bf16 value as the amax, against exact search
+    bits = np.arange(1, 0x7F80, dtype=np.uint16)
+    got = quant.ue8m0_scale(widen(bits))
+    step = 97   # the exact search is slow in Python: every 97th pattern plus the extremes
+    for b in list(range(1, 0x7F80, step)) + [1, 2, 0x7F7F, 0x7F7E, 0x0080, 0x007F]:
+        want = exact_pow2_scale(bf16_value(b))
+        assert Fraction(float(got[b - 1])) == want, (hex(b), got[b - 1], want)
+    # every result is a power of two, not below amax/448, and its half is below
+    a = widen(bits).astype(np.float64)
+    s = got.astype(np.float64)
+    m, _ = np.frexp(s)
+    assert np.all(m == 0.5)
+    assert np.all(s * 448.0 >= a)
+    clamped = s == 2.0 ** -127
+    assert np.all((s / 2 * 448.0 < a) | clamped)
+
+
+def test_ue8m0_scale_closed_forms():
+    for k in range(-120, 120):
+        a = np.float32(448.0 * 2.0 ** k)
+        assert quant.ue8m0_scale(np.array([a]))[0] == np.float32(2.0 ** k), k
+        up = np.float32(a * (1 + 2.0 ** -7))           # the next bf16 value up
+        assert quant.ue8m0_scale(np.array([up]))[0] == np.float32(2.0 ** (k + 1)), k
+        down = np.float32(a * (1 - 2.0 ** -8))         # the next bf16 value down (1.75 -> 1.7421875)
+        assert quant.ue8m0_scale(np.array([down]))[0] == np.float32(2.0 ** k), k
+    assert quant.ue8m0_scale(np.array([np.float32(0.0)]))[0] == 0.0
+    assert quant.ue8m0_scale(np.array([np.float32(1e-38)]))[0] == np.float32(2.0 ** -127)
+
+
+def test_ue8m0_block_quant_properties():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((64, 512)) * np.exp(rng.uniform(-20, 20, (64, 1)))
+    bits = synth.f64_to_bf16_bits(x)
+    bits[3, 128:256] = 0                            # zero block
+    q, s = quant.act_quant_block_ue8m0(bits)
+    xf = widen(bits).reshape(64, 4, 128).astype(np.float64)
+    sd = s.astype(np.float64)
+    assert s[3, 1] == 0 and not q[3, 128:256].any()
+    nz = sd > 0
+    m, _ = np.frexp(sd[nz])
+    assert np.all(m == 0.5)
+    # codes are the nearest e4m3 (ties to even) of the exact quotient x / s
+    y = np.where(nz[..., None], xf / np.where(nz, sd, 1.0)[..., None], 0.0)
+    assert np.all(np.abs(y) <= 448.0)
+    want = nearest_code_vec(y.astype(np.float32).reshape(64, 512))
+    want[3, 128:256] = 0
+    assert np.array_equal(q, want)
+    # the block's largest code lies in (224, 448] (scale within a factor 2 of amax/448)
+    dec = np.abs(e4m3.DECODE[q].reshape(64, 4, 128))
+    assert np.all(dec.max(axis=2)[nz] > 224.0 * (1 - 2.0 ** -4))
+
+
+def test_ue8m0_fraction_bruteforce():
+    rng = np.random.default_rng(12)
+    for t in range(6):
+        bits = synth.f64_to_bf16_bits(rng.standard_normal(128) * 10.0 ** rng.uniform(-30, 30))
+        q, s = quant.act_quant_block_ue8m0(bits.reshape(1, 128))
+        vals = [bf16_value(b) for b in bits]
+        sw = exact_pow2_scale(max(abs(v) for v in vals))
+        assert Fraction(float(s[0, 0])) == sw
+        for i, (b, v) in enumerate(zip(bits, vals)):
+            assert q[0, i] == nearest_e4m3(fl32(v / sw), negative=bool(int(b) & 0x8000)), (t, i)
+
+
+def test_ue8m0_matches_fp32_rule_when_scale_is_power_of_two():
+    # amax / 448 a power of two: both rules give the same scale and codes
+    rng = np.random.default_rng(13)
+    x = rng.uniform(-1, 1, (16, 256))
+    x[:, 0] = 448.0 * 2.0 ** rng.integers(-30, 30, 16)     # the amax of block 0
+    x[:, 128] = -3.5 * 2.0 ** rng.integers(-30, 30, 16)     # and of block 1 (3.5 = 448 / 128)
+    x[:, 1:128] *= np.abs(x[:, :1]) / 2
+    x[:, 129:] *= np.abs(x[:, 128:129]) / 2
+    bits = synth.f64_to_bf16_bits(x)
+    q1, s1 = quant.act_quant_block(bits)
+    q2, s2 = quant.act_quant_block_ue8m0(bits)
+    assert np.array_equal(s1, s2) and np.array_equal(q1, q2)
+
+
+def test_ue8m0_weight_blocks():
+    rng = np.random.default_rng(14)
+    w = synth.f64_to_bf16_bits(rng.standard_normal((256, 384)) * 0.02)
+    q, s = quant.weight_quant_block_ue8m0(w)
+    assert q.shape == (256, 384) and s.shape == (2, 3)
+    for bn in range(2):
+        for bk in range(3):
+            blk = w[bn * 128:(bn + 1) * 128, bk * 128:(bk + 1) * 128]
+            qb, sb = quant.act_quant_block_ue8m0(blk.reshape(1, -1), block=128 * 128)
+            assert sb[0, 0] == s[bn, bk]
+            assert np.array_equal(qb.reshape(128, 128), q[bn * 128:(bn + 1) * 128, bk * 128:(bk + 1) * 128])
