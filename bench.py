@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--rotate", type=int, default=0,
                    help="input copies rotated across steps (0: enough copies for >= 512 MiB of distinct "
                         "inputs, twice the last-level cache, capped at 64)")
+    p.add_argument("--scale-fmt", default="fp32", choices=["fp32", "ue8m0"],
+                   help="block scales: amax/448 (fp32) or powers of two (ue8m0: act-quant and weight quant "
+                        "with power-of-two scales, GEMM with the matrix cores applying them)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=None, help="rows of the CPU oracle sample")
     return p.parse_args()
@@ -143,9 +146,15 @@ class Workload:
         self.M, self.N, self.K = M, N, K
         rot = self.rot = rotation(2 * M * K + N * K)
         a = bf16(d["a"])
-        wq, wsc = fb.fp8_weight_quant_block(bf16(d["w"]))
+        ue = args.scale_fmt == "ue8m0"
+        act_q = fb.fp8_act_quant_block_ue8m0 if ue else fb.fp8_act_quant_block
+        gemm_f = fb.fp8_gemm_blockscaled_ue8m0 if ue else fb.fp8_gemm_blockscaled
+        wq, wsc = (fb.fp8_weight_quant_block_ue8m0 if ue else fb.fp8_weight_quant_block)(bf16(d["w"]))
         if "w_scale" in d:
-            wsc = torch.from_numpy(d["w_scale"]).to(dev)
+            ws_host = d["w_scale"]
+            if ue:   # the drawn scales, rounded up to powers of two
+                ws_host = np.ldexp(np.float32(1.0), np.ceil(np.log2(ws_host)).astype(np.int32)).astype(np.float32)
+            wsc = torch.from_numpy(ws_host).to(dev)
         a_s = [a] + [a.clone() for _ in range(rot - 1)]
         w_s = [wq] + [wq.clone() for _ in range(rot - 1)]
         qa = [torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev) for _ in range(rot)]
@@ -154,7 +163,7 @@ class Workload:
         gwsb = fb.fp8_gemm_blockscaled_workspace_bytes(M, N, K)
         gws = torch.empty((max(gwsb, 16),), dtype=torch.uint8, device=dev)
         self.stages.append(("act_quant_block",
-                            lambda i: fb.fp8_act_quant_block(a_s[i % rot], out=(qa[i % rot], sa[i % rot])),
+                            lambda i: act_q(a_s[i % rot], out=(qa[i % rot], sa[i % rot])),
                             2 * M * K + M * K + 4 * (M * K // 128), 0))
         if w == "c5":
             qt = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
@@ -166,9 +175,11 @@ class Workload:
                                 3 * M * K + 4, 0))
         gemm_bytes = M * K + 4 * M * (K // 128) + N * K + 4 * (N // 128) * (K // 128) + 2 * M * N
         self.stages.append(("gemm_blockscaled",
-                            lambda i: fb.fp8_gemm_blockscaled(qa[i % rot], sa[i % rot], w_s[i % rot], wsc,
-                                                              out=c, workspace=gws),
+                            lambda i: gemm_f(qa[i % rot], sa[i % rot], w_s[i % rot], wsc,
+                                             out=c, workspace=gws),
                             gemm_bytes, 2 * M * N * K))
+        if ue:
+            wl += " (power-of-two block scales)"
         self.config = {"workload": wl, "M": M, "N": N, "K": K}
         self.cpu = (w, M, K, N)
 
@@ -243,7 +254,7 @@ def time_steps(torch, wl, steps, warmup, graph):
     return step_ms, per_stage, wall
 
 
-def cpu_baseline(wl, rows_arg):
+def cpu_baseline(wl, rows_arg, ue8m0=False):
     """The oracle, as it stands, on a bounded row sample of the same workload."""
     import synth
     from oracle import gemm as ogemm, quant as oquant
@@ -265,11 +276,11 @@ def cpu_baseline(wl, rows_arg):
     d = {"c1": lambda: synth.gen_c1(), "c3": lambda: synth.gen_c3(M), "c4": lambda: synth.gen_c4(),
          "c5": lambda: synth.gen_c5()}[kind]()
     a = d["a"][:rows]
-    qw, sw = oquant.weight_quant_block(d["w"])          # offline step, not timed
+    qw, sw = (oquant.weight_quant_block_ue8m0 if ue8m0 else oquant.weight_quant_block)(d["w"])  # offline
     if "w_scale" in d:
         sw = d["w_scale"]
     t0 = time.perf_counter()
-    qa, sa = oquant.act_quant_block(a)
+    qa, sa = (oquant.act_quant_block_ue8m0 if ue8m0 else oquant.act_quant_block)(a)
     if kind == "c5":
         oquant.amax_quant_tensor(a)
     ogemm.gemm_blockscaled_ref(qa, sa, qw, sw)
@@ -320,7 +331,8 @@ def main():
     ds = stages[dominant]
     if per_stage is not None:
         src = "gemm.hip" if dominant == "gemm_blockscaled" else "quant.hip"
-        traffic = load_traffic(f"{dominant}:{args.workload}", src)
+        fmt = "_ue8m0" if args.scale_fmt == "ue8m0" and dominant != "amax_quant_tensor" else ""
+        traffic = load_traffic(f"{dominant}{fmt}:{args.workload}", src)
         if dominant == "gemm_blockscaled" and 2 * wl.M * wl.N * wl.K / max(ds["algorithmic_bytes"], 1) > 625:
             roofline = {"bound": "mfma", "achieved": ds["TFLOP/s"], "peak": FP8_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": ds["TFLOP/s"] / FP8_PEAK_TFLOPS, "traffic": traffic}
@@ -339,7 +351,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline and wl.cpu is not None:
-        cpu = cpu_baseline(wl, args.cpu_rows)
+        cpu = cpu_baseline(wl, args.cpu_rows, ue8m0=args.scale_fmt == "ue8m0")
         cpu["host_cpus"] = os.cpu_count()
         try:
             cpu["affinity_cpus"] = len(os.sched_getaffinity(0))

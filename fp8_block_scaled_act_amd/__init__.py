@@ -10,6 +10,8 @@ Entry points (same names as the C ABI):
     fp8_amax_quant_tensor(x)         -> (q, s)   any shape; s fp32 [1]
     fp8_gemm_blockscaled(a, sa, w, sw) -> c      c bf16 [M, N] = A . W^T
     fp8_weight_quant_block(w)        -> (q, s)   w bf16 [N, K]; s fp32 [N/128, K/128]
+    fp8_act_quant_block_ue8m0, fp8_weight_quant_block_ue8m0, fp8_gemm_blockscaled_ue8m0:
+                                     the same with power-of-two scales
 ``q`` tensors are ``torch.float8_e4m3fn`` (the OCP e4m3 "fn" bytes). Each
 function also accepts preallocated outputs (``out=``) so that a caller can
 time or graph-capture calls without allocations.
@@ -31,6 +33,9 @@ __all__ = [
     "fp8_gemm_blockscaled",
     "fp8_gemm_blockscaled_workspace_bytes",
     "fp8_weight_quant_block",
+    "fp8_act_quant_block_ue8m0",
+    "fp8_weight_quant_block_ue8m0",
+    "fp8_gemm_blockscaled_ue8m0",
     "debug_encode_e4m3",
     "EXPORTED_SYMBOLS",
 ]
@@ -48,6 +53,9 @@ EXPORTED_SYMBOLS = (
     "fp8_gemm_blockscaled_workspace_bytes",
     "fp8_gemm_blockscaled",
     "fp8_weight_quant_block",
+    "fp8_act_quant_block_ue8m0",
+    "fp8_weight_quant_block_ue8m0",
+    "fp8_gemm_blockscaled_ue8m0",
     "fp8bs_debug_encode_e4m3",
 )
 
@@ -90,6 +98,12 @@ def lib() -> ctypes.CDLL:
     L.fp8_gemm_blockscaled.restype = ctypes.c_int
     L.fp8_weight_quant_block.argtypes = [vp, i64, i64, vp, fp, vp]
     L.fp8_weight_quant_block.restype = ctypes.c_int
+    L.fp8_act_quant_block_ue8m0.argtypes = [vp, i64, i64, vp, fp, vp]
+    L.fp8_act_quant_block_ue8m0.restype = ctypes.c_int
+    L.fp8_weight_quant_block_ue8m0.argtypes = [vp, i64, i64, vp, fp, vp]
+    L.fp8_weight_quant_block_ue8m0.restype = ctypes.c_int
+    L.fp8_gemm_blockscaled_ue8m0.argtypes = [vp, fp, vp, fp, vp, i64, i64, i64, vp, sz, vp]
+    L.fp8_gemm_blockscaled_ue8m0.restype = ctypes.c_int
     L.fp8bs_debug_encode_e4m3.argtypes = [fp, vp, i64, vp]
     L.fp8bs_debug_encode_e4m3.restype = ctypes.c_int
     _lib = L
@@ -122,8 +136,7 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def fp8_act_quant_block(x: torch.Tensor, out=None):
-    """1x128 block quantization of bf16 ``x`` [M, K] (K % 128 == 0)."""
+def _act_quant(fn: str, x: torch.Tensor, out):
     _need(x, "x", torch.bfloat16)
     if x.dim() != 2:
         raise ValueError("x must be 2-D [M, K]")
@@ -134,9 +147,19 @@ def fp8_act_quant_block(x: torch.Tensor, out=None):
     else:
         q, s = out
     with torch.cuda.device(x.device):
-        rc = lib().fp8_act_quant_block(_ptr(x), M, K, _ptr(q), _ptr(s), ctypes.c_void_p(_stream(x.device)))
-    _check("fp8_act_quant_block", rc)
+        rc = getattr(lib(), fn)(_ptr(x), M, K, _ptr(q), _ptr(s), ctypes.c_void_p(_stream(x.device)))
+    _check(fn, rc)
     return q, s
+
+
+def fp8_act_quant_block(x: torch.Tensor, out=None):
+    """1x128 block quantization of bf16 ``x`` [M, K] (K % 128 == 0)."""
+    return _act_quant("fp8_act_quant_block", x, out)
+
+
+def fp8_act_quant_block_ue8m0(x: torch.Tensor, out=None):
+    """1x128 block quantization with power-of-two scales."""
+    return _act_quant("fp8_act_quant_block_ue8m0", x, out)
 
 
 def fp8_amax_quant_tensor_workspace_bytes(numel: int) -> int:
@@ -171,9 +194,7 @@ def _as_u8(t):
     return t.view(torch.uint8) if t.dtype == E4M3 else t
 
 
-def fp8_gemm_blockscaled(a, a_scale, w, w_scale, out=None, workspace=None):
-    """C = A . W^T (bf16 [M, N]) from e4m3 A [M, K] with 1x128 scales and e4m3
-    W [N, K] with 128x128 scales."""
+def _gemm(fn, a, a_scale, w, w_scale, out, workspace):
     for t, n in ((a, "a"), (w, "w")):
         if t.dtype not in (E4M3, torch.uint8):
             raise TypeError(f"{n} must be float8_e4m3fn (or its uint8 bytes)")
@@ -193,15 +214,25 @@ def fp8_gemm_blockscaled(a, a_scale, w, w_scale, out=None, workspace=None):
     if workspace is None and wsb > 0:
         workspace = torch.empty((wsb,), dtype=torch.uint8, device=a.device)
     with torch.cuda.device(a.device):
-        rc = lib().fp8_gemm_blockscaled(
+        rc = getattr(lib(), fn)(
             _ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(c), M, N, K, _ptr(workspace),
             workspace.numel() if workspace is not None else 0, ctypes.c_void_p(_stream(a.device)))
-    _check("fp8_gemm_blockscaled", rc)
+    _check(fn, rc)
     return c
 
 
-def fp8_weight_quant_block(w: torch.Tensor, out=None):
-    """128x128 block quantization of a bf16 weight [N, K]."""
+def fp8_gemm_blockscaled(a, a_scale, w, w_scale, out=None, workspace=None):
+    """C = A . W^T (bf16 [M, N]) from e4m3 A [M, K] with 1x128 scales and e4m3
+    W [N, K] with 128x128 scales."""
+    return _gemm("fp8_gemm_blockscaled", a, a_scale, w, w_scale, out, workspace)
+
+
+def fp8_gemm_blockscaled_ue8m0(a, a_scale, w, w_scale, out=None, workspace=None):
+    """As fp8_gemm_blockscaled, for power-of-two scales (applied by the matrix cores)."""
+    return _gemm("fp8_gemm_blockscaled_ue8m0", a, a_scale, w, w_scale, out, workspace)
+
+
+def _weight_quant(fn, w: torch.Tensor, out):
     _need(w, "w", torch.bfloat16)
     if w.dim() != 2:
         raise ValueError("w must be 2-D [N, K]")
@@ -212,9 +243,19 @@ def fp8_weight_quant_block(w: torch.Tensor, out=None):
     else:
         q, s = out
     with torch.cuda.device(w.device):
-        rc = lib().fp8_weight_quant_block(_ptr(w), N, K, _ptr(q), _ptr(s), ctypes.c_void_p(_stream(w.device)))
-    _check("fp8_weight_quant_block", rc)
+        rc = getattr(lib(), fn)(_ptr(w), N, K, _ptr(q), _ptr(s), ctypes.c_void_p(_stream(w.device)))
+    _check(fn, rc)
     return q, s
+
+
+def fp8_weight_quant_block(w: torch.Tensor, out=None):
+    """128x128 block quantization of a bf16 weight [N, K]."""
+    return _weight_quant("fp8_weight_quant_block", w, out)
+
+
+def fp8_weight_quant_block_ue8m0(w: torch.Tensor, out=None):
+    """128x128 block quantization with power-of-two scales."""
+    return _weight_quant("fp8_weight_quant_block_ue8m0", w, out)
 
 
 def debug_encode_e4m3(v: torch.Tensor, out=None):

@@ -42,6 +42,21 @@ __device__ __forceinline__ v4f mfma_16x16x128_fp8(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// The matrix cores' own block scaling: D = (A * 2^(sa-127)) . (B * 2^(sb-127)) + C,
+// the scale bytes (e8m0) per lane, each applying to that lane's row or column
+// and 32-element K slice. Used when the block scales are powers of two.
+__device__ __forceinline__ v4f mfma_16x16x128_fp8_scaled(const v8i& a, const v8i& b, const v4f& c, int sa,
+                                                        int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// e8m0 byte of a power-of-two float scale: its biased exponent (2^-127, a
+// subnormal, and 0.0 both give 0, i.e. 2^-127; a zero scale only ever
+// multiplies all-zero codes)
+__device__ __forceinline__ int e8m0_byte(float s) {
+  return static_cast<int>((__float_as_uint(s) >> 23) & 0xFFu);
+}
+
 __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
   const f2 v = {lo, hi};
   const bf2 r = __builtin_convertvector(v, bf2);
@@ -156,7 +171,9 @@ struct TileCfg {
   static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS");
 };
 
-template <int BN, int BM, int WN, int WM, int STAGES, int WAVES_PER_EU>
+// HW: block scales are powers of two, applied by the matrix cores (no scale
+// FMAs; the fp32 accumulator is the MFMA's own, chained over the K blocks)
+template <int BN, int BM, int WN, int WM, int STAGES, int WAVES_PER_EU, bool HW>
 __global__ __launch_bounds__(64 * WN * WM) __attribute__((amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void gemm_blockscaled_tiled_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
@@ -275,11 +292,14 @@ void gemm_blockscaled_tiled_kernel(
   v8i wlast;
   v4f pp[NJ];
   float csl[NJ];
+  int sal[NJ];          // HW: e8m0 activation scales of the last row's block
+  int swl = 127;        // HW: e8m0 weight scale of the last row's block
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     af[j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
     pp[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     csl[j] = 0.0f;
+    sal[j] = 127;
   }
   wlast = v8i{0, 0, 0, 0, 0, 0, 0, 0};
   // copies of the prefetched block: kPerRow per MFMA row, rows 0..kDmaRows-1
@@ -328,6 +348,43 @@ void gemm_blockscaled_tiled_kernel(
       sav[0] = v.x; sav[1] = v.y;
     }
     v8i wcur = lds_frag(st, wrow, c0);
+    if constexpr (HW) {
+      // last row of block kb-1 (its scales in swl, sal); each A fragment is
+      // refilled right after its MFMA
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        acc[NI - 1][j] = mfma_16x16x128_fp8_scaled(wlast, af[j], acc[NI - 1][j], swl, sal[j]);
+        af[j] = lds_frag(sA, arow + j * 16, c0);
+      }
+      v8i wnext = lds_frag(st, wrow + 16, c0);
+      const int swb8 = e8m0_byte(swb);
+      int sab[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) sab[j] = e8m0_byte(sav[j]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[0][j] = mfma_16x16x128_fp8_scaled(wcur, af[j], acc[0][j], swb8, sab[j]);
+      if constexpr (PF) {
+#pragma unroll
+        for (int p = 0; p < kPerRow; ++p)
+          if (p < kPer) issue_part(kb + STAGES - 1, p);
+      }
+#pragma unroll
+      for (int i = 1; i < NI - 1; ++i) {
+        wcur = wnext;
+        wnext = lds_frag(st, wrow + (i + 1) * 16, c0);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_16x16x128_fp8_scaled(wcur, af[j], acc[i][j], swb8, sab[j]);
+        if constexpr (PF) {
+#pragma unroll
+          for (int p = i * kPerRow; p < (i + 1) * kPerRow; ++p)
+            if (p < kPer) issue_part(kb + STAGES - 1, p);
+        }
+      }
+      wlast = wnext;
+      swl = swb8;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) sal[j] = sab[j];
+    } else {
     // last row of block kb-1; each A fragment is refilled right after its MFMA
     v4f pc[NJ];
 #pragma unroll
@@ -379,13 +436,18 @@ void gemm_blockscaled_tiled_kernel(
     wlast = wnext;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) csl[j] = cs[j];
+    }
     __builtin_amdgcn_sched_barrier(0);
     swb = swrow[min(kb + 1, KB - 1)];
   };
   const int kb_pf = max(KB - (STAGES - 1), 0);
   for (int kb = 0; kb < kb_pf; ++kb) step(kb, std::true_type{});
   for (int kb = kb_pf; kb < KB; ++kb) step(kb, std::false_type{});
-  {
+  if constexpr (HW) {
+    // last row of the last block
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[NI - 1][j] = mfma_16x16x128_fp8_scaled(wlast, af[j], acc[NI - 1][j], swl, sal[j]);
+  } else {
     // last row of the last block
     v4f pc[NJ];
 #pragma unroll
@@ -757,14 +819,14 @@ int launch_decode(const uint8_t* a, const float* sa, const uint8_t* w, const flo
 #define FP8BS_GEMM_TILE 0
 #endif
 
-template <int BN, int BM, int WN, int WM, int STAGES, int WPE>
+template <int BN, int BM, int WN, int WM, int STAGES, int WPE, bool HW>
 int launch_tiled(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c,
                  int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int64_t tiles_m = (M + BM - 1) / BM;
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t grid = (tiles_m * tiles_n + 7) / 8 * 8;
   if (grid > 0x7FFFFFF0LL) return FP8BS_ERR_SHAPE;
-  hipLaunchKernelGGL((gemm_blockscaled_tiled_kernel<BN, BM, WN, WM, STAGES, WPE>),
+  hipLaunchKernelGGL((gemm_blockscaled_tiled_kernel<BN, BM, WN, WM, STAGES, WPE, HW>),
                      dim3(static_cast<unsigned>(grid)), dim3(64 * WN * WM), 0, st, a, sa, w, sw, c,
                      M, N, K, static_cast<int>(tiles_m), static_cast<int>(tiles_n));
   return FP8BS_OK;
@@ -782,9 +844,14 @@ size_t fp8_gemm_blockscaled_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return use_decode(M) && M > kDecStreamMaxM ? decode_workspace_bytes(M, N, K) : 0;
 }
 
-int fp8_gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m3,
-                         const float* w_scale, void* c_bf16, int64_t M, int64_t N, int64_t K,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace fp8bs {
+namespace {
+template <bool HW>
+int gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m3, const float* w_scale,
+                     void* c_bf16, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   if (!a_e4m3 || !a_scale || !w_e4m3 || !w_scale || !c_bf16) return FP8BS_ERR_NULL;
   if (M < 1 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
   if (M > (INT64_MAX / K) || M > (INT64_MAX / N) || N > (INT64_MAX / K)) return FP8BS_ERR_SHAPE;
@@ -804,6 +871,8 @@ int fp8_gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w
   hipStream_t st = as_stream(stream);
   (void)hipGetLastError();
   int rc;
+  // decode shapes are bound by streaming W: the FMA kernels serve both scale
+  // formats (with power-of-two scales the scale product is exact there too)
   if (use_decode(M)) {
     if (M <= kDecStreamMaxM)
       rc = launch_decode_stream(a, a_scale, w, w_scale, c, M, N, K, st);
@@ -817,18 +886,37 @@ int fp8_gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w
   // else 128 x 128 tiles (two workgroups per CU)
   const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles256 >= dev.num_cus)
-    rc = launch_tiled<256, 256, 2, 4, 2, 2>(a, a_scale, w, w_scale, c, M, N, K, st);
+    rc = launch_tiled<256, 256, 2, 4, 2, 2, HW>(a, a_scale, w, w_scale, c, M, N, K, st);
   else
-    rc = launch_tiled<128, 128, 2, 2, 2, 2>(a, a_scale, w, w_scale, c, M, N, K, st);
+    rc = launch_tiled<128, 128, 2, 2, 2, 2, HW>(a, a_scale, w, w_scale, c, M, N, K, st);
 #elif FP8BS_GEMM_TILE == 1
-  rc = launch_tiled<128, 128, 2, 2, 2, 2>(a, a_scale, w, w_scale, c, M, N, K, st);
+  rc = launch_tiled<128, 128, 2, 2, 2, 2, HW>(a, a_scale, w, w_scale, c, M, N, K, st);
 #elif FP8BS_GEMM_TILE == 2
-  rc = launch_tiled<256, 256, 2, 4, 2, 2>(a, a_scale, w, w_scale, c, M, N, K, st);
+  rc = launch_tiled<256, 256, 2, 4, 2, 2, HW>(a, a_scale, w, w_scale, c, M, N, K, st);
 #elif FP8BS_GEMM_TILE == 3
-  rc = launch_tiled<256, 128, 2, 2, 3, 1>(a, a_scale, w, w_scale, c, M, N, K, st);
+  rc = launch_tiled<256, 128, 2, 2, 3, 1, HW>(a, a_scale, w, w_scale, c, M, N, K, st);
 #endif
   if (rc != FP8BS_OK) return rc;
   return launch_status();
+}
+
+}  // namespace
+}  // namespace fp8bs
+
+extern "C" {
+
+int fp8_gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m3,
+                         const float* w_scale, void* c_bf16, int64_t M, int64_t N, int64_t K,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_blockscaled<false>(a_e4m3, a_scale, w_e4m3, w_scale, c_bf16, M, N, K, workspace,
+                                 workspace_bytes, stream);
+}
+
+int fp8_gemm_blockscaled_ue8m0(const void* a_e4m3, const float* a_scale, const void* w_e4m3,
+                               const float* w_scale, void* c_bf16, int64_t M, int64_t N, int64_t K,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_blockscaled<true>(a_e4m3, a_scale, w_e4m3, w_scale, c_bf16, M, N, K, workspace,
+                                workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -15,13 +15,6 @@
 #include "device_common.h"
 #include "host_common.h"
 
-#ifndef FP8BS_AQ_BPG
-#define FP8BS_AQ_BPG 1
-#endif
-#ifndef FP8BS_AQ_NT
-#define FP8BS_AQ_NT 0
-#endif
-
 namespace fp8bs {
 namespace {
 
@@ -34,12 +27,6 @@ constexpr int kThreads = 256;
 // block amax is a 3-step DPP max inside the 8-lane group.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ void store_nt2(uint2 v, uint2* p) {
-  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 w = {v.x, v.y};
-  __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
-}
-
 // quantize the 8 bf16 of a uint4 with scale s (and r = 1/s on the fast path)
 template <bool kFast>
 __device__ __forceinline__ uint2 quant8(const uint4 v, float s, float r) {
@@ -50,39 +37,56 @@ __device__ __forceinline__ uint2 quant8(const uint4 v, float s, float r) {
   return make_uint2(pack4_e4m3(f[0], f[1], f[2], f[3]), pack4_e4m3(f[4], f[5], f[6], f[7]));
 }
 
-// BPG blocks per 8-lane group (all loads issued first); NT: codes stored
-// non-temporally
-template <int BPG, bool NT>
+// Power-of-two scale (the ue8m0 variants): the smallest 2^e >= amax/448 with
+// e >= -127, read off amax's bits (amax > 0). With amax = m * 2^E, m in [1, 2)
+// and 448 = 1.75 * 2^8: e = E - 8 if m <= 1.75, else E - 7; subnormal amax
+// (below 2^-126) gives e < -127, so -127. Also r = 2^-e (e <= 120 for bf16
+// inputs, so r is a normal float): x / s is then the exact product x * r,
+// rounded only where it leaves the normal range, like the division.
+__device__ __forceinline__ void pow2_scale(float amax, float& s, float& r) {
+  const uint32_t b = __float_as_uint(amax);
+  const int ef = static_cast<int>((b >> 23) & 0xFFu);
+  int e = ef == 0 ? -127 : ef - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  e = e < -127 ? -127 : e;
+  s = e >= -126 ? __uint_as_float(static_cast<uint32_t>(e + 127) << 23) : __uint_as_float(0x00400000u);
+  r = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+}
+
+__device__ __forceinline__ uint2 quant8_pow2(const uint4 v, float r) {
+  float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] *= r;
+  return make_uint2(pack4_e4m3(f[0], f[1], f[2], f[3]), pack4_e4m3(f[4], f[5], f[6], f[7]));
+}
+
+// P2: power-of-two scales (ue8m0) instead of amax/448
+template <bool P2>
 __global__ __launch_bounds__(kThreads) void act_quant_block_kernel(
     const uint4* __restrict__ x, uint2* __restrict__ q, float* __restrict__ scale,
     int64_t nblocks) {
-  const int64_t grp = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 3;
+  const int64_t blk = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 3;
   const int sub = threadIdx.x & 7;
-  const int64_t blk0 = grp * BPG;
-  if (blk0 >= nblocks) return;  // whole 8-lane groups leave together
+  if (blk >= nblocks) return;  // whole 8-lane groups leave together
 
-  uint4 v[BPG][2];
-#pragma unroll
-  for (int b = 0; b < BPG; ++b) {
-    const int64_t blk = blk0 + b;
-    if (BPG == 1 || blk < nblocks) {
-      v[b][0] = x[blk * 16 + sub];
-      v[b][1] = x[blk * 16 + 8 + sub];
-    }
-  }
-#pragma unroll
-  for (int b = 0; b < BPG; ++b) {
-    const int64_t blk = blk0 + b;
-    if (BPG > 1 && blk >= nblocks) break;   // uniform over the group
-    const uint4 v0 = v[b][0], v1 = v[b][1];
-    float m = 0.0f;
-    m = absmax2(v0.x, m); m = absmax2(v0.y, m); m = absmax2(v0.z, m); m = absmax2(v0.w, m);
-    m = absmax2(v1.x, m); m = absmax2(v1.y, m); m = absmax2(v1.z, m); m = absmax2(v1.w, m);
-    const float amax = group8_max(m);
+  const uint4 v0 = x[blk * 16 + sub];
+  const uint4 v1 = x[blk * 16 + 8 + sub];
 
-    const float s = div_ieee(amax, kE4m3Max);
+  float m = 0.0f;
+  m = absmax2(v0.x, m); m = absmax2(v0.y, m); m = absmax2(v0.z, m); m = absmax2(v0.w, m);
+  m = absmax2(v1.x, m); m = absmax2(v1.y, m); m = absmax2(v1.z, m); m = absmax2(v1.w, m);
+  const float amax = group8_max(m);
+
+  float s;
+  uint2 o0, o1;
+  if constexpr (P2) {
+    float r;
+    pow2_scale(amax, s, r);
+    o0 = quant8_pow2(v0, r);
+    o1 = quant8_pow2(v1, r);
+  } else {
+    s = div_ieee(amax, kE4m3Max);
     const bool fast = s >= kFastScaleMin;
-    uint2 o0, o1;
     if (__builtin_expect(__ballot(!fast) == 0, 1)) {
       const float r = div_ieee(1.0f, s);
       o0 = quant8<true>(v0, s, r);
@@ -91,25 +95,22 @@ __global__ __launch_bounds__(kThreads) void act_quant_block_kernel(
       o0 = quant8<false>(v0, s, 0.0f);
       o1 = quant8<false>(v1, s, 0.0f);
     }
-    if (amax == 0.0f) {  // all-zero block: scale 0, codes 0x00
-      o0 = make_uint2(0u, 0u);
-      o1 = make_uint2(0u, 0u);
-    }
-    if constexpr (NT) {
-      store_nt2(o0, q + blk * 16 + sub);
-      store_nt2(o1, q + blk * 16 + 8 + sub);
-    } else {
-      q[blk * 16 + sub] = o0;
-      q[blk * 16 + 8 + sub] = o1;
-    }
-    if (sub == 0) scale[blk] = s;
   }
+  if (amax == 0.0f) {  // all-zero block: scale 0, codes 0x00
+    s = 0.0f;
+    o0 = make_uint2(0u, 0u);
+    o1 = make_uint2(0u, 0u);
+  }
+  q[blk * 16 + sub] = o0;
+  q[blk * 16 + 8 + sub] = o1;
+  if (sub == 0) scale[blk] = s;
 }
 
 // ---------------------------------------------------------------------------
 // 128x128 weight blocks: one workgroup per block. Thread t covers row t/2,
 // columns [64*(t%2), 64*(t%2)+64) as 8 uint4.
 // ---------------------------------------------------------------------------
+template <bool P2>
 __global__ __launch_bounds__(kThreads) void weight_quant_block_kernel(
     const uint16_t* __restrict__ w, uint8_t* __restrict__ q, float* __restrict__ scale,
     int64_t K) {
@@ -133,17 +134,26 @@ __global__ __launch_bounds__(kThreads) void weight_quant_block_kernel(
   __syncthreads();
   const float amax = fmaxf(fmaxf(wave_max_lds[0], wave_max_lds[1]),
                            fmaxf(wave_max_lds[2], wave_max_lds[3]));
-  const float s = div_ieee(amax, kE4m3Max);
+  float s;
   uint2 o[8];
-  if (s >= kFastScaleMin) {  // uniform across the workgroup
-    const float r = div_ieee(1.0f, s);
+  if constexpr (P2) {
+    float r;
+    pow2_scale(amax, s, r);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = quant8<true>(v[i], s, r);
+    for (int i = 0; i < 8; ++i) o[i] = quant8_pow2(v[i], r);
   } else {
+    s = div_ieee(amax, kE4m3Max);
+    if (s >= kFastScaleMin) {  // uniform across the workgroup
+      const float r = div_ieee(1.0f, s);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = quant8<false>(v[i], s, 0.0f);
+      for (int i = 0; i < 8; ++i) o[i] = quant8<true>(v[i], s, r);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = quant8<false>(v[i], s, 0.0f);
+    }
   }
   if (amax == 0.0f) {
+    s = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = make_uint2(0u, 0u);
   }
@@ -373,8 +383,12 @@ const char* fp8bs_status_string(int status) {
   }
 }
 
-int fp8_act_quant_block(const void* x_bf16, int64_t M, int64_t K, void* q_e4m3, float* scale,
-                        void* stream) {
+}  // extern "C"
+
+namespace fp8bs {
+namespace {
+template <bool P2>
+int act_quant_block(const void* x_bf16, int64_t M, int64_t K, void* q_e4m3, float* scale, void* stream) {
   if (!x_bf16 || !q_e4m3 || !scale) return FP8BS_ERR_NULL;
   if (M < 1 || K < 128 || K % 128 != 0) return FP8BS_ERR_SHAPE;
   if (M > (INT64_MAX / K)) return FP8BS_ERR_SHAPE;
@@ -382,19 +396,17 @@ int fp8_act_quant_block(const void* x_bf16, int64_t M, int64_t K, void* q_e4m3, 
   const DeviceInfo dev = current_device();
   if (dev.status != FP8BS_OK) return dev.status;
   const int64_t nblocks = M * (K / 128);
-  constexpr int kBpg = FP8BS_AQ_BPG;
-  const int64_t groups = (nblocks + kBpg - 1) / kBpg;
-  const int64_t grid = (groups * 8 + kThreads - 1) / kThreads;
+  const int64_t grid = (nblocks * 8 + kThreads - 1) / kThreads;
   if (grid > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
   (void)hipGetLastError();
-  hipLaunchKernelGGL((act_quant_block_kernel<kBpg, FP8BS_AQ_NT != 0>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kThreads), 0, as_stream(stream), static_cast<const uint4*>(x_bf16),
-                     static_cast<uint2*>(q_e4m3), scale, nblocks);
+  hipLaunchKernelGGL((act_quant_block_kernel<P2>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
+                     as_stream(stream), static_cast<const uint4*>(x_bf16), static_cast<uint2*>(q_e4m3),
+                     scale, nblocks);
   return launch_status();
 }
 
-int fp8_weight_quant_block(const void* w_bf16, int64_t N, int64_t K, void* q_e4m3, float* scale,
-                           void* stream) {
+template <bool P2>
+int weight_quant_block(const void* w_bf16, int64_t N, int64_t K, void* q_e4m3, float* scale, void* stream) {
   if (!w_bf16 || !q_e4m3 || !scale) return FP8BS_ERR_NULL;
   if (N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
   if (N / 128 > 65535 || K / 128 > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
@@ -402,11 +414,35 @@ int fp8_weight_quant_block(const void* w_bf16, int64_t N, int64_t K, void* q_e4m
   const DeviceInfo dev = current_device();
   if (dev.status != FP8BS_OK) return dev.status;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(weight_quant_block_kernel,
+  hipLaunchKernelGGL((weight_quant_block_kernel<P2>),
                      dim3(static_cast<unsigned>(K / 128), static_cast<unsigned>(N / 128)),
                      dim3(kThreads), 0, as_stream(stream), static_cast<const uint16_t*>(w_bf16),
                      static_cast<uint8_t*>(q_e4m3), scale, K);
   return launch_status();
+}
+}  // namespace
+}  // namespace fp8bs
+
+extern "C" {
+
+int fp8_act_quant_block(const void* x_bf16, int64_t M, int64_t K, void* q_e4m3, float* scale,
+                        void* stream) {
+  return act_quant_block<false>(x_bf16, M, K, q_e4m3, scale, stream);
+}
+
+int fp8_act_quant_block_ue8m0(const void* x_bf16, int64_t M, int64_t K, void* q_e4m3, float* scale,
+                              void* stream) {
+  return act_quant_block<true>(x_bf16, M, K, q_e4m3, scale, stream);
+}
+
+int fp8_weight_quant_block(const void* w_bf16, int64_t N, int64_t K, void* q_e4m3, float* scale,
+                           void* stream) {
+  return weight_quant_block<false>(w_bf16, N, K, q_e4m3, scale, stream);
+}
+
+int fp8_weight_quant_block_ue8m0(const void* w_bf16, int64_t N, int64_t K, void* q_e4m3, float* scale,
+                                 void* stream) {
+  return weight_quant_block<true>(w_bf16, N, K, q_e4m3, scale, stream);
 }
 
 size_t fp8_amax_quant_tensor_workspace_bytes(int64_t numel) {

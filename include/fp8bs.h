@@ -135,6 +135,38 @@ int fp8_weight_quant_block(const void* w_bf16, int64_t N, int64_t K,
                            void* q_e4m3, float* scale, void* stream);
 
 /*
+ * Power-of-two ("ue8m0") scale variants. The DeepSeek-V3 page's activation
+ * quantization benchmark ("How to Profile DeepSeek-V3 Inference Kernels
+ * Using Triton Autotuning", section "Benchmarking the Activation Quantization
+ * Kernel") runs act_quant_kernel with scale_fmt="ue8m0"; the page gives no
+ * formula, and the reading taken here is the smallest power of two not below
+ * amax/448:
+ *     s = 2^e,  e = max(ceil(log2(amax / 448)), -127)   (exact; 0 if amax == 0)
+ *     q = e4m3_rne(clamp(fl32(x / s), -448, 448))
+ * so that |x/s| <= 448 still holds and dequantization is exact. Scales are
+ * written as fp32 (powers of two), layouts and errors as in the fp32-scale
+ * functions above.
+ */
+int fp8_act_quant_block_ue8m0(const void* x_bf16, int64_t M, int64_t K,
+                              void* q_e4m3, float* scale, void* stream);
+int fp8_weight_quant_block_ue8m0(const void* w_bf16, int64_t N, int64_t K,
+                                 void* q_e4m3, float* scale, void* stream);
+
+/*
+ * Block-scaled FP8 GEMM for power-of-two block scales (as the ue8m0
+ * quantizers write them; 0.0 is allowed for all-zero blocks): C = A . W^T with
+ * the arguments, layouts, workspace and errors of fp8_gemm_blockscaled. For
+ * M > 64 the scales are applied by the matrix cores themselves (e8m0 scale
+ * operands of the FP8 MFMA; the fp32 accumulator is the MFMA's own across the
+ * K blocks), so no per-block scale FMA runs. Scales that are not powers of
+ * two are outside the contract (only their exponent would be used).
+ */
+int fp8_gemm_blockscaled_ue8m0(const void* a_e4m3, const float* a_scale,
+                               const void* w_e4m3, const float* w_scale,
+                               void* c_bf16, int64_t M, int64_t N, int64_t K,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Test hook: the library's own fp32 -> e4m3 rounding step (clamp to +-448,
  * round to nearest even, sign kept), applied elementwise, so that it can be
  * checked exhaustively against a reference encoder.

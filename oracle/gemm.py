@@ -35,6 +35,15 @@ dequantized operands, ``gemm_exp_envelope_ref``) bounds it, the 2**-19 term
 covering the 24-bit combining steps. Without the floor no kernel that
 accumulates in finite precision can meet 4 ulp where cancellation makes |R|
 much smaller than S.
+
+When the matrix cores also apply the (power-of-two) block scales and carry
+the fp32 accumulator from one K block to the next as their own accumulator
+input, the add of each block into that accumulator is not one rounded fp32
+add: each of the up to 8 run-pair sums of a block is added with truncation at
+2**(exponent of the accumulator - 24) (measured: eight products of 2**-26 in
+eight separate runs vanish next to an accumulator of 1.0), so a block can lose
+up to 8 * 2**(e_acc - 24) < 2**-20 * |acc| <= 2**-20 * S. For that path the
+accumulation term is tau_chained(K) = (K/128 + 1) * 2**-20 in place of tau(K).
 """
 from __future__ import annotations
 
@@ -140,11 +149,19 @@ def gemm_tolerance_tau(K: int) -> float:
     return (K // BLOCK + 2) * 2.0 ** -24 + 2.0 ** -20
 
 
-def compare_gemm(c_bits: np.ndarray, R: np.ndarray, S: np.ndarray, K: int, Se: np.ndarray):
+def gemm_tolerance_tau_chained(K: int) -> float:
+    """Accumulation term when the matrix cores carry the accumulator over the
+    K blocks (module docstring)."""
+    return (K // BLOCK + 1) * 2.0 ** -20
+
+
+def compare_gemm(c_bits: np.ndarray, R: np.ndarray, S: np.ndarray, K: int, Se: np.ndarray,
+                 chained: bool = False):
     """Check a bf16 GEMM result against the fp64 reference.
 
     Returns a dict with the normwise error, the worst elementwise ratio
-    |C-R| / (4 ulp + TAU_MATRIX Se + tau S) and a boolean ``ok``.
+    |C-R| / (4 ulp + TAU_MATRIX Se + tau S) and a boolean ``ok``; ``chained``
+    selects tau_chained (matrix cores carrying the accumulator over K blocks).
     """
     C = bf16_bits_to_f64(c_bits)
     R = np.asarray(R, dtype=np.float64)
@@ -153,7 +170,8 @@ def compare_gemm(c_bits: np.ndarray, R: np.ndarray, S: np.ndarray, K: int, Se: n
     err = np.abs(C - R)
     rmax = float(np.max(np.abs(R))) if R.size else 0.0
     normwise = float(np.max(err)) / rmax if rmax > 0 else float(np.max(err, initial=0.0))
-    bound = 4.0 * ulp_bf16(R) + TAU_MATRIX * Se + gemm_tolerance_tau(K) * S
+    tau = gemm_tolerance_tau_chained(K) if chained else gemm_tolerance_tau(K)
+    bound = 4.0 * ulp_bf16(R) + TAU_MATRIX * Se + tau * S
     ratio = float(np.max(err / bound)) if err.size else 0.0
     return dict(normwise=normwise, elem_ratio=ratio,
                 ok=bool(normwise <= 1e-2 and ratio <= 1.0))

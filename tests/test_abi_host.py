@@ -124,3 +124,13 @@ def test_gemm_k_limits(L):
     assert L.fp8_gemm_blockscaled(P, P, P, P, P, 32, 128, 128 * 513, None, 0, None) == ESHAPE
     assert L.fp8_gemm_blockscaled_workspace_bytes(8, 2048, 7168) == 0
     assert L.fp8_gemm_blockscaled_workspace_bytes(32, 2048, 7168) > 0
+
+
+def test_ue8m0_argument_errors(L):
+    assert L.fp8_act_quant_block_ue8m0(None, 4, 128, P, P, None) == ENULL
+    assert L.fp8_act_quant_block_ue8m0(P, 4, 100, P, P, None) == ESHAPE
+    assert L.fp8_weight_quant_block_ue8m0(P, 64, 128, P, P, None) == ESHAPE
+    f = L.fp8_gemm_blockscaled_ue8m0
+    assert f(None, P, P, P, P, 4, 128, 128, None, 0, None) == ENULL
+    assert f(P, P, P, P, P, 4, 100, 128, None, 0, None) == ESHAPE
+    assert f(PU, P, P, P, P, 4, 128, 128, None, 0, None) == EALIGN

@@ -15,6 +15,7 @@ Independent checks:
 from fractions import Fraction
 
 import numpy as np
+import pytest
 import torch
 
 from oracle import e4m3, gemm
@@ -114,7 +115,8 @@ def normal_codes(rng, shape, scale):
     return e4m3.encode(v)
 
 
-def test_compare_accepts_reference_and_rejects_wrong_results():
+@pytest.mark.parametrize("chained", [False, True])
+def test_compare_accepts_reference_and_rejects_wrong_results(chained):
     rng = np.random.default_rng(6)
     M, N, K = 8, 256, 512
     qa, qw = normal_codes(rng, (M, K), 100.0), normal_codes(rng, (N, K), 100.0)
@@ -124,22 +126,27 @@ def test_compare_accepts_reference_and_rejects_wrong_results():
     S = gemm.gemm_abs_ref(qa, sa, qw, sw)
     Se = gemm.gemm_exp_envelope_ref(qa, sa, qw, sw)
     good = gemm.f64_to_bf16_rne(R)
-    res = gemm.compare_gemm(good, R, S, K, Se)
+    cmp = lambda c: gemm.compare_gemm(c, R, S, K, Se, chained=chained)
+    res = cmp(good)
     assert res["ok"], res
     # one activation block scale lost
     sa_bad = sa.copy(); sa_bad[:, 2] = 1.0
     bad = gemm.f64_to_bf16_rne(gemm.gemm_blockscaled_ref(qa, sa_bad, qw, sw))
-    assert not gemm.compare_gemm(bad, R, S, K, Se)["ok"]
+    assert not cmp(bad)["ok"]
     # transposed weight blocks
     bad = gemm.f64_to_bf16_rne(gemm.gemm_blockscaled_ref(qa, sa, qw, sw[::-1]))
-    assert not gemm.compare_gemm(bad, R, S, K, Se)["ok"]
+    assert not cmp(bad)["ok"]
     # one K block dropped
     qa_bad = qa.copy(); qa_bad[:, 128:256] = 0
     bad = gemm.f64_to_bf16_rne(gemm.gemm_blockscaled_ref(qa_bad, sa, qw, sw))
-    assert not gemm.compare_gemm(bad, R, S, K, Se)["ok"]
-    # a result off by 2**-8 relative everywhere
+    assert not cmp(bad)["ok"]
+    # a result off by 2**-6 relative everywhere
     bad = gemm.f64_to_bf16_rne(R * (1 + 2.0 ** -6))
-    assert not gemm.compare_gemm(bad, R, S, K, Se)["ok"]
+    assert not cmp(bad)["ok"]
+    # a power-of-two scale off by one exponent in one block
+    sw_bad = sw.copy(); sw_bad[0, 1] *= 2
+    bad = gemm.f64_to_bf16_rne(gemm.gemm_blockscaled_ref(qa, sa, qw, sw_bad))
+    assert not cmp(bad)["ok"]
 
 
 def test_exp_envelope_closed_form():
