@@ -171,3 +171,17 @@ def weight_quant_block_ue8m0(w_bits: np.ndarray, block: int = 128):
     q, s = _quant_groups_ue8m0(wf.reshape(nb * kb, block * block))
     q = q.reshape(nb, kb, block, block).transpose(0, 2, 1, 3).reshape(N, K)
     return np.ascontiguousarray(q), s.reshape(nb, kb)
+
+
+def act_quant_block_f32(x: np.ndarray, block: int = 128):
+    """1x128 block quantization of a float32 [M, K] tensor (the DeepSeek-V3
+    page's ``act_quant`` example quantizes a float32 tensor: section
+    "Benchmarking the Activation Quantization Kernel"). Same rule as
+    ``act_quant_block`` with the float32 values as they are (finite inputs).
+    """
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    M, K = x.shape
+    if K % block:
+        raise ValueError("K must be a multiple of the block size")
+    q, s = _quant_groups(x.reshape(M * (K // block), block))
+    return q.reshape(M, K), s.reshape(M, K // block)

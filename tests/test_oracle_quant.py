@@ -357,3 +357,47 @@ def test_ue8m0_weight_blocks():
             qb, sb = quant.act_quant_block_ue8m0(blk.reshape(1, -1), block=128 * 128)
             assert sb[0, 0] == s[bn, bk]
             assert np.array_equal(qb.reshape(128, 128), q[bn * 128:(bn + 1) * 128, bk * 128:(bk + 1) * 128])
+
+
+
+# --------------------------------------------------------------------------
+# float32 input
+
+def brute_group_f32(vals32):
+    vals = [Fraction(float(v)) for v in vals32]
+    amax = max(abs(v) for v in vals)
+    s = fl32(amax / 448)
+    if s == 0:
+        return 0.0, [0] * len(vals)
+    return float(s), [nearest_e4m3(fl32(v / s), negative=bool(np.signbit(v32)))
+                      for v, v32 in zip(vals, vals32)]
+
+
+def test_f32_input_fraction_bruteforce():
+    rng = np.random.default_rng(31)
+    for t in range(5):
+        x = (rng.standard_normal(128) * 10.0 ** rng.uniform(-35, 35)).astype(np.float32)
+        x[3] = -x[3]
+        q, s = quant.act_quant_block_f32(x.reshape(1, 128))
+        sw, codes = brute_group_f32(x)
+        assert float(s[0, 0]) == sw
+        assert list(q[0]) == codes, t
+
+
+def test_f32_input_reduces_to_bf16_rule_on_bf16_values():
+    # float32 values that are bf16 values quantize exactly as the bf16 path
+    bits = synth.gen_c1()["a"]
+    q1, s1 = quant.act_quant_block(bits)
+    q2, s2 = quant.act_quant_block_f32(widen(bits))
+    assert np.array_equal(q1, q2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+
+
+def test_f32_input_full_precision_matters():
+    # values with more than 8 significant bits: the quotient uses all of them
+    x = np.full((1, 128), np.float32(1.0), np.float32)
+    x[0, 0] = np.float32(448.0)                       # amax -> scale exactly 1.0
+    x[0, 1] = np.float32(1.0625 + 2.0 ** -20)         # just above the tie 1.0625 (between 1.0 and 1.125)
+    x[0, 2] = np.float32(1.0625)                      # the tie itself: to even (1.0, code 0x38)
+    q, s = quant.act_quant_block_f32(x)
+    assert s[0, 0] == 1.0
+    assert q[0, 1] == 0x39 and q[0, 2] == 0x38
