@@ -42,8 +42,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="c5", choices=["c5", "c4", "c3", "c2", "c1", "copy"],
-                   help="copy: a plain 256 MiB device-to-device copy (HBM reference for counters)")
+    p.add_argument("--workload", default="c5", choices=["c5", "c4", "c3", "c2", "c1", "aq32", "copy"],
+                   help="copy: a plain 256 MiB device-to-device copy (HBM reference for counters); "
+                        "aq32: block act-quant of the prefill activation given as float32")
     p.add_argument("--M", type=int, default=None, help="rows for c2/c3")
     p.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
     p.add_argument("--rotate", type=int, default=0,
@@ -128,6 +129,21 @@ class Workload:
             self.config = {"workload": f"per-tensor dynamic quant, X bf16 [{M}, {K}]", "M": M, "K": K}
             self.M, self.N, self.K = M, 0, K
             self.cpu = ("c2", M, K, None)
+            return
+
+        if w == "aq32":
+            M, K = 4096, 7168
+            xf = torch.from_numpy(synth.bf16_bits_to_f64(synth.gen_c4()["a"]).astype(np.float32)).to(dev)
+            rot = self.rot = rotation(4 * M * K)
+            xs = [xf] + [xf.clone() for _ in range(rot - 1)]
+            q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+            s = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+            self.stages.append(("act_quant_block_f32",
+                                lambda i: fb.fp8_act_quant_block_f32(xs[i % rot], out=(q, s)),
+                                4 * M * K + M * K + 4 * (M * K // 128), 0))
+            self.config = {"workload": f"block act-quant of float32 X [{M}, {K}]", "M": M, "K": K}
+            self.M, self.N, self.K = M, 0, K
+            self.cpu = ("aq32", M, K, None)
             return
 
         if w == "c1":
@@ -265,6 +281,13 @@ def cpu_baseline(wl, rows_arg, ue8m0=False):
         blas_threads = os.cpu_count() or 1
     kind, M, K, N = wl.cpu
     t = 0.0
+    if kind == "aq32":
+        rows = min(M, rows_arg or 1024)
+        x = synth.bf16_bits_to_f64(synth.gen_c4()["a"][:rows]).astype(np.float32)
+        t0 = time.perf_counter(); oquant.act_quant_block_f32(x); t = time.perf_counter() - t0
+        value = (5 * rows * K + 4 * rows * (K // 128)) / t / 1e9
+        return {"value": value, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"block quant of float32 [{rows}, {K}] (numpy, one thread), {t:.2f} s"}
     if kind == "c2":
         rows = min(M, rows_arg or M)
         x = synth.gen_c2(rows)["x"]

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
     fp8_weight_quant_block(w)        -> (q, s)   w bf16 [N, K]; s fp32 [N/128, K/128]
     fp8_act_quant_block_ue8m0, fp8_weight_quant_block_ue8m0, fp8_gemm_blockscaled_ue8m0:
                                      the same with power-of-two scales
+    fp8_act_quant_block_f32(x)       -> (q, s)   x fp32 [M, K]
 ``q`` tensors are ``torch.float8_e4m3fn`` (the OCP e4m3 "fn" bytes). Each
 function also accepts preallocated outputs (``out=``) so that a caller can
 time or graph-capture calls without allocations.
@@ -36,6 +37,7 @@ __all__ = [
     "fp8_act_quant_block_ue8m0",
     "fp8_weight_quant_block_ue8m0",
     "fp8_gemm_blockscaled_ue8m0",
+    "fp8_act_quant_block_f32",
     "debug_encode_e4m3",
     "EXPORTED_SYMBOLS",
 ]
@@ -56,6 +58,7 @@ EXPORTED_SYMBOLS = (
     "fp8_act_quant_block_ue8m0",
     "fp8_weight_quant_block_ue8m0",
     "fp8_gemm_blockscaled_ue8m0",
+    "fp8_act_quant_block_f32",
     "fp8bs_debug_encode_e4m3",
 )
 
@@ -104,6 +107,8 @@ def lib() -> ctypes.CDLL:
     L.fp8_weight_quant_block_ue8m0.restype = ctypes.c_int
     L.fp8_gemm_blockscaled_ue8m0.argtypes = [vp, fp, vp, fp, vp, i64, i64, i64, vp, sz, vp]
     L.fp8_gemm_blockscaled_ue8m0.restype = ctypes.c_int
+    L.fp8_act_quant_block_f32.argtypes = [fp, i64, i64, vp, fp, vp]
+    L.fp8_act_quant_block_f32.restype = ctypes.c_int
     L.fp8bs_debug_encode_e4m3.argtypes = [fp, vp, i64, vp]
     L.fp8bs_debug_encode_e4m3.restype = ctypes.c_int
     _lib = L
@@ -136,8 +141,8 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def _act_quant(fn: str, x: torch.Tensor, out):
-    _need(x, "x", torch.bfloat16)
+def _act_quant(fn: str, x: torch.Tensor, out, dtype=torch.bfloat16):
+    _need(x, "x", dtype)
     if x.dim() != 2:
         raise ValueError("x must be 2-D [M, K]")
     M, K = x.shape
@@ -160,6 +165,11 @@ def fp8_act_quant_block(x: torch.Tensor, out=None):
 def fp8_act_quant_block_ue8m0(x: torch.Tensor, out=None):
     """1x128 block quantization with power-of-two scales."""
     return _act_quant("fp8_act_quant_block_ue8m0", x, out)
+
+
+def fp8_act_quant_block_f32(x: torch.Tensor, out=None):
+    """1x128 block quantization of float32 ``x`` [M, K]."""
+    return _act_quant("fp8_act_quant_block_f32", x, out, dtype=torch.float32)
 
 
 def fp8_amax_quant_tensor_workspace_bytes(numel: int) -> int:

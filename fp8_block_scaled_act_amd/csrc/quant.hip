@@ -106,6 +106,34 @@ __global__ __launch_bounds__(kThreads) void act_quant_block_kernel(
   if (sub == 0) scale[blk] = s;
 }
 
+// float32 input: eight lanes per 1x128 block (512 bytes), lane `sub` holding
+// the float4 chunks sub, sub+8, sub+16 and sub+24, so each 16-byte load of a
+// wave reads eight whole 128-byte quarters of blocks. The quotient is the
+// IEEE division: the reciprocal-based form used for bf16 inputs is proven
+// exact only for 8-bit significands.
+__global__ __launch_bounds__(kThreads) void act_quant_block_f32_kernel(
+    const float4* __restrict__ x, uint32_t* __restrict__ q, float* __restrict__ scale, int64_t nblocks) {
+  const int64_t blk = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 3;
+  const int sub = threadIdx.x & 7;
+  if (blk >= nblocks) return;  // whole 8-lane groups leave together
+  float4 v[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v[c] = x[blk * 32 + sub + 8 * c];
+  float m = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    m = fmaxf(fmaxf(fmaxf(m, fabsf(v[c].x)), fmaxf(fabsf(v[c].y), fabsf(v[c].z))), fabsf(v[c].w));
+  const float amax = group8_max(m);
+  const float s = div_ieee(amax, kE4m3Max);
+  const bool zero = amax == 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint32_t o = pack4_e4m3(div_ieee(v[c].x, s), div_ieee(v[c].y, s), div_ieee(v[c].z, s), div_ieee(v[c].w, s));
+    q[blk * 32 + sub + 8 * c] = zero ? 0u : o;
+  }
+  if (sub == 0) scale[blk] = s;
+}
+
 // ---------------------------------------------------------------------------
 // 128x128 weight blocks: one workgroup per block. Thread t covers row t/2,
 // columns [64*(t%2), 64*(t%2)+64) as 8 uint4.
@@ -433,6 +461,24 @@ int fp8_act_quant_block(const void* x_bf16, int64_t M, int64_t K, void* q_e4m3, 
 int fp8_act_quant_block_ue8m0(const void* x_bf16, int64_t M, int64_t K, void* q_e4m3, float* scale,
                               void* stream) {
   return act_quant_block<true>(x_bf16, M, K, q_e4m3, scale, stream);
+}
+
+int fp8_act_quant_block_f32(const float* x_f32, int64_t M, int64_t K, void* q_e4m3, float* scale,
+                            void* stream) {
+  if (!x_f32 || !q_e4m3 || !scale) return FP8BS_ERR_NULL;
+  if (M < 1 || K < 128 || K % 128 != 0) return FP8BS_ERR_SHAPE;
+  if (M > (INT64_MAX / K)) return FP8BS_ERR_SHAPE;
+  if (!aligned(x_f32, 16) || !aligned(q_e4m3, 16) || !aligned(scale, 4)) return FP8BS_ERR_ALIGN;
+  const DeviceInfo dev = current_device();
+  if (dev.status != FP8BS_OK) return dev.status;
+  const int64_t nblocks = M * (K / 128);
+  const int64_t grid = (nblocks * 8 + kThreads - 1) / kThreads;
+  if (grid > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(act_quant_block_f32_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
+                     as_stream(stream), reinterpret_cast<const float4*>(x_f32), static_cast<uint32_t*>(q_e4m3),
+                     scale, nblocks);
+  return launch_status();
 }
 
 int fp8_weight_quant_block(const void* w_bf16, int64_t N, int64_t K, void* q_e4m3, float* scale,

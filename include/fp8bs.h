@@ -68,6 +68,20 @@ int fp8_act_quant_block(const void* x_bf16, int64_t M, int64_t K,
                         void* q_e4m3, float* scale, void* stream);
 
 /*
+ * The same 1x128 block quantization of float32 input (the DeepSeek-V3 page's
+ * act_quant example quantizes a float32 tensor: "How to Profile DeepSeek-V3
+ * Inference Kernels Using Triton Autotuning", section "Benchmarking the
+ * Activation Quantization Kernel"), with the rule above over the float32
+ * values as given.
+ *
+ *   x_f32   [M, K] fp32, 16-byte aligned            (input, finite)
+ *   q_e4m3  [M, K] e4m3 bytes, 16-byte aligned      (output)
+ *   scale   [M, K/128] fp32, 4-byte aligned         (output)
+ */
+int fp8_act_quant_block_f32(const float* x_f32, int64_t M, int64_t K,
+                            void* q_e4m3, float* scale, void* stream);
+
+/*
  * Per-tensor dynamic quantization: one scale from the exact amax over all
  * numel elements. TensorRT-LLM PR "Size the per-tensor FP8 dynamic-quant amax
  * grid to the input" (sections "Description" and "Correctness"): an exact

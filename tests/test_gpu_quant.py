@@ -141,3 +141,25 @@ def test_signed_zeros_in_nonzero_blocks():
     torch.cuda.synchronize()
     q_ref, s_ref = quant.amax_quant_tensor(bits)
     assert np.array_equal(to_u8(q), q_ref) and to_f32(s)[0] == s_ref
+
+
+def check_block_f32(x, label):
+    fb = binding()
+    say("act_quant_block_f32", label, x.shape)
+    q, s = fb.fp8_act_quant_block_f32(torch.from_numpy(np.ascontiguousarray(x, np.float32)).to("cuda:0"))
+    torch.cuda.synchronize()
+    q_ref, s_ref = quant.act_quant_block_f32(x)
+    assert np.array_equal(to_f32(s).view(np.uint32), s_ref.view(np.uint32)), label
+    bad = np.argwhere(to_u8(q) != q_ref)
+    assert bad.shape[0] == 0, (label, bad[:5].tolist())
+
+
+def test_block_quant_f32_input():
+    rng = np.random.default_rng(41)
+    x = (rng.standard_normal((257, 1024)) * np.exp(rng.uniform(-40, 40, (257, 1)))).astype(np.float32)
+    x[5, 128:256] = 0.0                                  # zero block
+    x[6, :128] = -0.0
+    x[7, 256:384] *= np.float32(1e-30)                   # small scales
+    x[8, :128] = np.float32(448.0) * (1 + rng.integers(0, 2, 128) * 2.0 ** -20)   # near-ties
+    check_block_f32(x, "f32 mixed")
+    check_block_f32(rng.standard_normal((1024, 128)).astype(np.float32), "f32 [1024, 128] (the page's example shape)")
