@@ -175,3 +175,20 @@ def compare_gemm(c_bits: np.ndarray, R: np.ndarray, S: np.ndarray, K: int, Se: n
     ratio = float(np.max(err / bound)) if err.size else 0.0
     return dict(normwise=normwise, elem_ratio=ratio,
                 ok=bool(normwise <= 1e-2 and ratio <= 1.0))
+
+
+def gemm_tensorscaled_ref(qa, sa, qw, sw):
+    """C = sa * sw * (dec(A) . dec(W)^T) in float64, for one scale per tensor
+    (the per-tensor dynamic quantization's output feeding the projection GEMM:
+    TensorRT-LLM PR "Size the per-tensor FP8 dynamic-quant amax grid to the
+    input", section "Description": the quantize step runs ahead of the GEMM and
+    hands it the quantized input and the scale). sa and sw are scalars."""
+    A = e4m3.DECODE[np.asarray(qa)].astype(np.float64)
+    W = e4m3.DECODE[np.asarray(qw)].astype(np.float64)
+    return float(np.float32(sa)) * float(np.float32(sw)) * (A @ W.T)
+
+
+def gemm_tensorscaled_abs_ref(qa, sa, qw, sw):
+    A = np.abs(e4m3.DECODE[np.asarray(qa)].astype(np.float64))
+    W = np.abs(e4m3.DECODE[np.asarray(qw)].astype(np.float64))
+    return abs(float(np.float32(sa)) * float(np.float32(sw))) * (A @ W.T)

@@ -179,3 +179,27 @@ def test_rows_sampler_matches_full():
     assert np.all(np.abs(r - R[rows, cols]) <= K * 2.0 ** -52 * S[rows, cols])
     assert np.all(np.abs(s - S[rows, cols]) <= K * 2.0 ** -52 * S[rows, cols])
     assert np.all(np.abs(se - Se[rows, cols]) <= K * 2.0 ** -52 * Se[rows, cols])
+
+
+
+def test_tensorscaled_ref_is_block_ref_with_constant_blocks():
+    rng = np.random.default_rng(51)
+    M, N, K = 9, 256, 384
+    qa, qw = normal_codes(rng, (M, K), 50.0), normal_codes(rng, (N, K), 50.0)
+    sa, sw = np.float32(0.0371), np.float32(2.5e-4)
+    R1 = gemm.gemm_tensorscaled_ref(qa, sa, qw, sw)
+    R2 = gemm.gemm_blockscaled_ref(qa, np.full((M, K // 128), sa, np.float32), qw,
+                                   np.full((N // 128, K // 128), sw, np.float32))
+    assert np.allclose(R1, R2, rtol=1e-14, atol=0)
+    S1 = gemm.gemm_tensorscaled_abs_ref(qa, sa, qw, sw)
+    assert np.all(S1 >= np.abs(R1))
+
+
+def test_tensorscaled_ref_integer_bruteforce():
+    # integer-valued codes and power-of-two scales: exact in int64
+    rng = np.random.default_rng(52)
+    ints = np.array([0x38, 0x40, 0x44, 0x48, 0x4A, 0xB8, 0xC0, 0x00], np.uint8)   # 1,2,3,4,5,-1,-2,0
+    qa = rng.choice(ints, (4, 256)); qw = rng.choice(ints, (128, 256))
+    A = e4m3.DECODE[qa].astype(np.int64); W = e4m3.DECODE[qw].astype(np.int64)
+    want = (A @ W.T).astype(np.float64) * 0.25 * 8.0
+    assert np.array_equal(gemm.gemm_tensorscaled_ref(qa, np.float32(0.25), qw, np.float32(8.0)), want)
