@@ -50,9 +50,10 @@ def parse():
     p.add_argument("--rotate", type=int, default=0,
                    help="input copies rotated across steps (0: enough copies for >= 512 MiB of distinct "
                         "inputs, twice the last-level cache, capped at 64)")
-    p.add_argument("--scale-fmt", default="fp32", choices=["fp32", "ue8m0"],
+    p.add_argument("--scale-fmt", default="fp32", choices=["fp32", "ue8m0", "tensor"],
                    help="block scales: amax/448 (fp32) or powers of two (ue8m0: act-quant and weight quant "
-                        "with power-of-two scales, GEMM with the matrix cores applying them)")
+                        "with power-of-two scales, GEMM with the matrix cores applying them); tensor: "
+                        "one scale per tensor (per-tensor quant of A, then the per-tensor-scaled GEMM)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=None, help="rows of the CPU oracle sample")
     return p.parse_args()
@@ -162,6 +163,29 @@ class Workload:
         self.M, self.N, self.K = M, N, K
         rot = self.rot = rotation(2 * M * K + N * K)
         a = bf16(d["a"])
+        if args.scale_fmt == "tensor":
+            wq, wsc = fb.fp8_amax_quant_tensor(bf16(d["w"]))
+            a_s = [a] + [a.clone() for _ in range(rot - 1)]
+            w_s = [wq] + [wq.clone() for _ in range(rot - 1)]
+            qa = [torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev) for _ in range(rot)]
+            sa = [torch.empty((1,), dtype=torch.float32, device=dev) for _ in range(rot)]
+            twsb = fb.fp8_amax_quant_tensor_workspace_bytes(M * K)
+            tws = torch.zeros((max(twsb, 16),), dtype=torch.uint8, device=dev)
+            c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            gwsb = fb.fp8_gemm_blockscaled_workspace_bytes(M, N, K)
+            gws = torch.empty((max(gwsb, 16),), dtype=torch.uint8, device=dev)
+            self.stages.append(("amax_quant_tensor",
+                                lambda i: fb.fp8_amax_quant_tensor(a_s[i % rot], out=(qa[i % rot], sa[i % rot]),
+                                                                   workspace=tws),
+                                3 * M * K + 4, 0))
+            self.stages.append(("gemm_blockscaled",
+                                lambda i: fb.fp8_gemm_tensorscaled(qa[i % rot], sa[i % rot], w_s[i % rot], wsc,
+                                                                   out=c, workspace=gws),
+                                M * K + N * K + 8 + 2 * M * N, 2 * M * N * K))
+            wl += " (one scale per tensor: per-tensor quant of A, per-tensor-scaled GEMM)"
+            self.config = {"workload": wl, "M": M, "N": N, "K": K}
+            self.cpu = None
+            return
         ue = args.scale_fmt == "ue8m0"
         act_q = fb.fp8_act_quant_block_ue8m0 if ue else fb.fp8_act_quant_block
         gemm_f = fb.fp8_gemm_blockscaled_ue8m0 if ue else fb.fp8_gemm_blockscaled

@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
     fp8_act_quant_block_ue8m0, fp8_weight_quant_block_ue8m0, fp8_gemm_blockscaled_ue8m0:
                                      the same with power-of-two scales
     fp8_act_quant_block_f32(x)       -> (q, s)   x fp32 [M, K]
+    fp8_gemm_tensorscaled(a, sa, w, sw) -> c     one scale per tensor (sa, sw [1])
 ``q`` tensors are ``torch.float8_e4m3fn`` (the OCP e4m3 "fn" bytes). Each
 function also accepts preallocated outputs (``out=``) so that a caller can
 time or graph-capture calls without allocations.
@@ -38,6 +39,7 @@ __all__ = [
     "fp8_weight_quant_block_ue8m0",
     "fp8_gemm_blockscaled_ue8m0",
     "fp8_act_quant_block_f32",
+    "fp8_gemm_tensorscaled",
     "debug_encode_e4m3",
     "EXPORTED_SYMBOLS",
 ]
@@ -59,6 +61,7 @@ EXPORTED_SYMBOLS = (
     "fp8_weight_quant_block_ue8m0",
     "fp8_gemm_blockscaled_ue8m0",
     "fp8_act_quant_block_f32",
+    "fp8_gemm_tensorscaled",
     "fp8bs_debug_encode_e4m3",
 )
 
@@ -109,6 +112,8 @@ def lib() -> ctypes.CDLL:
     L.fp8_gemm_blockscaled_ue8m0.restype = ctypes.c_int
     L.fp8_act_quant_block_f32.argtypes = [fp, i64, i64, vp, fp, vp]
     L.fp8_act_quant_block_f32.restype = ctypes.c_int
+    L.fp8_gemm_tensorscaled.argtypes = [vp, fp, vp, fp, vp, i64, i64, i64, vp, sz, vp]
+    L.fp8_gemm_tensorscaled.restype = ctypes.c_int
     L.fp8bs_debug_encode_e4m3.argtypes = [fp, vp, i64, vp]
     L.fp8bs_debug_encode_e4m3.restype = ctypes.c_int
     _lib = L
@@ -204,7 +209,7 @@ def _as_u8(t):
     return t.view(torch.uint8) if t.dtype == E4M3 else t
 
 
-def _gemm(fn, a, a_scale, w, w_scale, out, workspace):
+def _gemm(fn, a, a_scale, w, w_scale, out, workspace, per_tensor=False):
     for t, n in ((a, "a"), (w, "w")):
         if t.dtype not in (E4M3, torch.uint8):
             raise TypeError(f"{n} must be float8_e4m3fn (or its uint8 bytes)")
@@ -217,7 +222,10 @@ def _gemm(fn, a, a_scale, w, w_scale, out, workspace):
         raise ValueError("a must be [M, K] and w [N, K]")
     M, K = a.shape
     N = w.shape[0]
-    if a_scale.shape != (M, K // 128) or w_scale.shape != (N // 128, K // 128):
+    if per_tensor:
+        if a_scale.numel() != 1 or w_scale.numel() != 1:
+            raise ValueError("a_scale and w_scale must hold one value each")
+    elif a_scale.shape != (M, K // 128) or w_scale.shape != (N // 128, K // 128):
         raise ValueError("a_scale must be [M, K/128] and w_scale [N/128, K/128]")
     c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     wsb = fp8_gemm_blockscaled_workspace_bytes(M, N, K)
@@ -240,6 +248,12 @@ def fp8_gemm_blockscaled(a, a_scale, w, w_scale, out=None, workspace=None):
 def fp8_gemm_blockscaled_ue8m0(a, a_scale, w, w_scale, out=None, workspace=None):
     """As fp8_gemm_blockscaled, for power-of-two scales (applied by the matrix cores)."""
     return _gemm("fp8_gemm_blockscaled_ue8m0", a, a_scale, w, w_scale, out, workspace)
+
+
+def fp8_gemm_tensorscaled(a, a_scale, w, w_scale, out=None, workspace=None):
+    """C = a_scale * w_scale * (A . W^T) (bf16 [M, N]); one fp32 scale per
+    operand, as a one-element device tensor (fp8_amax_quant_tensor's output)."""
+    return _gemm("fp8_gemm_tensorscaled", a, a_scale, w, w_scale, out, workspace, per_tensor=True)
 
 
 def _weight_quant(fn, w: torch.Tensor, out):

@@ -171,9 +171,12 @@ struct TileCfg {
   static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS");
 };
 
-// HW: block scales are powers of two, applied by the matrix cores (no scale
-// FMAs; the fp32 accumulator is the MFMA's own, chained over the K blocks)
-template <int BN, int BM, int WN, int WM, int STAGES, int WAVES_PER_EU, bool HW>
+// MODE 0: fp32 block scales, one scale FMA per output and K block.
+// MODE 1: power-of-two block scales, applied by the matrix cores (no scale
+//         FMAs; the fp32 accumulator is the MFMA's own, chained over K).
+// MODE 2: one scale per tensor (sa[0], sw[0]): products accumulated by the
+//         matrix cores unscaled, the scale product applied in the epilogue.
+template <int BN, int BM, int WN, int WM, int STAGES, int WAVES_PER_EU, int MODE>
 __global__ __launch_bounds__(64 * WN * WM) __attribute__((amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void gemm_blockscaled_tiled_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
@@ -181,6 +184,8 @@ void gemm_blockscaled_tiled_kernel(
     int tiles_m, int tiles_n) {
   using T = TileCfg<BN, BM, WN, WM, STAGES>;
   constexpr int NI = T::NI, NJ = T::NJ;
+  constexpr bool HW = MODE >= 1;
+  constexpr bool TS = MODE == 2;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * T::kStageBytes];
 
   // XCD-aware tile order: the 8 XCDs take workgroups round-robin, so give
@@ -226,7 +231,7 @@ void gemm_blockscaled_tiled_kernel(
   const float* stile = sa + m0 * KB;
   // scale slot s = wave*64 + lane (first kSWaves waves) holds the scale of
   // row wq*TM + 16*j + l16, where s = wq*TM + l16*NJ + j
-  const bool loads_scales = wave < T::kSWaves;
+  const bool loads_scales = !TS && wave < T::kSWaves;
   uint32_t soff;
   {
     const int s = wave * 64 + lane;
@@ -280,7 +285,7 @@ void gemm_blockscaled_tiled_kernel(
   // fragment read of block kb and waited for right after the next barrier,
   // before the first fragment read: scalar loads complete out of order, so
   // while one is in flight every wait for an LDS read is a full wait.
-  float swb = swrow[0];
+  float swb = TS ? 1.0f : swrow[0];
   // Software pipeline across blocks. The MFMAs of the last W row of block
   // kb-1 are issued after the barrier that opens block kb, interleaved with
   // the reads of block kb's A fragments (each read refills the registers the
@@ -340,7 +345,11 @@ void gemm_blockscaled_tiled_kernel(
     const uint8_t* sA = st + T::kWBytes;
     const float* sv = reinterpret_cast<const float*>(st + T::kWBytes + T::kABytes) + wm * T::TM + (lane & 15) * NJ;
     float sav[NJ];
-    if constexpr (NJ == 4) {
+    if constexpr (TS) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) sav[j] = 1.0f;
+      (void)sv;
+    } else if constexpr (NJ == 4) {
       const float4 v = *reinterpret_cast<const float4*>(sv);
       sav[0] = v.x; sav[1] = v.y; sav[2] = v.z; sav[3] = v.w;
     } else {
@@ -357,10 +366,10 @@ void gemm_blockscaled_tiled_kernel(
         af[j] = lds_frag(sA, arow + j * 16, c0);
       }
       v8i wnext = lds_frag(st, wrow + 16, c0);
-      const int swb8 = e8m0_byte(swb);
+      const int swb8 = TS ? 127 : e8m0_byte(swb);
       int sab[NJ];
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) sab[j] = e8m0_byte(sav[j]);
+      for (int j = 0; j < NJ; ++j) sab[j] = TS ? 127 : e8m0_byte(sav[j]);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[0][j] = mfma_16x16x128_fp8_scaled(wcur, af[j], acc[0][j], swb8, sab[j]);
       if constexpr (PF) {
@@ -438,7 +447,7 @@ void gemm_blockscaled_tiled_kernel(
     for (int j = 0; j < NJ; ++j) csl[j] = cs[j];
     }
     __builtin_amdgcn_sched_barrier(0);
-    swb = swrow[min(kb + 1, KB - 1)];
+    if constexpr (!TS) swb = swrow[min(kb + 1, KB - 1)];
   };
   const int kb_pf = max(KB - (STAGES - 1), 0);
   for (int kb = 0; kb < kb_pf; ++kb) step(kb, std::true_type{});
@@ -470,6 +479,14 @@ void gemm_blockscaled_tiled_kernel(
   static_assert(BM * BN * 2 <= STAGES * T::kStageBytes, "C tile must fit the LDS ring");
   constexpr int kRowBytes = BN * 2;
   constexpr int kChunks = BN / 8;
+  if constexpr (TS) {
+    // the tensor scales' product, once per output (then the bf16 rounding)
+    const float st = sa[0] * sw[0];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] *= st;
+  }
   __syncthreads();   // every wave is done reading the last stage
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -515,8 +532,9 @@ void gemm_blockscaled_tiled_kernel(
 constexpr int kDecWaves = FP8BS_DEC_WAVES;
 constexpr int kDecStreamMaxM = 16;
 
-// MT: 16-row groups of A (M <= 16*MT); kDecDepth: K blocks in flight per wave
-template <int MT, int kDecDepth>
+// MT: 16-row groups of A (M <= 16*MT); kDecDepth: K blocks in flight per wave;
+// TS: one scale per tensor (sa[0] * sw[0] for every block)
+template <int MT, int kDecDepth, bool TS>
 __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(kDecWaves / 4, kDecWaves / 4)))
 void gemm_blockscaled_decode_stream_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
@@ -554,9 +572,10 @@ void gemm_blockscaled_decode_stream_kernel(
     for (int j = 0; j < MT; ++j) {
       aq[d][j][0] = *reinterpret_cast<const uint4*>(ap[j] + kb * kBK);
       aq[d][j][1] = *reinterpret_cast<const uint4*>(ap[j] + kb * kBK + 16);
-      sq[d][j] = sp[j][kb];
+      if constexpr (!TS) sq[d][j] = sp[j][kb];
     }
   };
+  const float cst = TS ? sa[0] * sw[0] : 0.0f;
 #pragma unroll
   for (int d = 0; d < kDecDepth; ++d)
     if (d < nt) load(d, d);
@@ -573,12 +592,12 @@ void gemm_blockscaled_decode_stream_kernel(
                            (int)wq[d][1].x, (int)wq[d][1].y, (int)wq[d][1].z, (int)wq[d][1].w};
         v8i af[MT];
         float cs[MT];
-        const float swb = swrow[wave + kDecWaves * t];
+        const float swb = TS ? 1.0f : swrow[wave + kDecWaves * t];
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
           af[j] = v8i{(int)aq[d][j][0].x, (int)aq[d][j][0].y, (int)aq[d][j][0].z, (int)aq[d][j][0].w,
                       (int)aq[d][j][1].x, (int)aq[d][j][1].y, (int)aq[d][j][1].z, (int)aq[d][j][1].w};
-          cs[j] = sq[d][j] * swb;
+          cs[j] = TS ? cst : sq[d][j] * swb;
         }
         if (t + kDecDepth < nt) load(d, t + kDecDepth);
 #pragma unroll
@@ -616,9 +635,10 @@ void gemm_blockscaled_decode_stream_kernel(
   }
 }
 
+template <bool TS>
 int launch_decode_stream(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c,
                          int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_blockscaled_decode_stream_kernel<1, 4>), dim3(static_cast<unsigned>(N / 16)),
+  hipLaunchKernelGGL((gemm_blockscaled_decode_stream_kernel<1, 4, TS>), dim3(static_cast<unsigned>(N / 16)),
                      dim3(64 * kDecWaves), 0, st, a, sa, w, sw, c, static_cast<int>(M), N, K);
   return FP8BS_OK;
 }
@@ -641,7 +661,7 @@ constexpr int kDecMaxM = 64;
 constexpr int kDecMaxSplits = 32;   // the reduction keeps one float4 per split in flight
 
 // MT: 16-row groups of A (M <= 16*MT); KBMAX: K blocks per split (LDS size)
-template <int MT, int KBMAX>
+template <int MT, int KBMAX, bool TS>
 __global__ __launch_bounds__(256) void gemm_blockscaled_decode_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, uint16_t* __restrict__ C, float* __restrict__ ws, int M, int64_t N,
@@ -703,12 +723,12 @@ __global__ __launch_bounds__(256) void gemm_blockscaled_decode_kernel(
           wq[d][0] = *reinterpret_cast<const uint4*>(wp + (k + kDecDepth) * kBK);
           wq[d][1] = *reinterpret_cast<const uint4*>(wp + (k + kDecDepth) * kBK + 16);
         }
-        const float swb = swrow[k];
+        const float swb = TS ? 1.0f : swrow[k];
 #pragma unroll
         for (int j = 0; j < MT; ++j) {
           const v8i af = lds_frag(lds + k * MP * 128, j * 16 + (lane & 15), c0);
           const v4f p = mfma_16x16x128_fp8(wf, af);
-          const float cs = sa[static_cast<int64_t>(mrow[j]) * KB + kb0 + k] * swb;
+          const float cs = TS ? sa[0] * sw[0] : sa[static_cast<int64_t>(mrow[j]) * KB + kb0 + k] * swb;
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(p[r], cs, acc[j][r]);
         }
@@ -785,6 +805,7 @@ size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return p.splits > 1 ? static_cast<size_t>(p.splits) * M * N * sizeof(float) : 0;
 }
 
+template <bool TS>
 int launch_decode(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c,
                   float* ws, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const DecodePlan p = decode_plan(N, K);
@@ -792,7 +813,7 @@ int launch_decode(const uint8_t* a, const float* sa, const uint8_t* w, const flo
   const int m = static_cast<int>(M);
   const int mt = (m + 15) / 16;
 #define FP8BS_DEC(MT, KBM)                                                                      \
-  hipLaunchKernelGGL((gemm_blockscaled_decode_kernel<MT, KBM>), grid, dim3(256), 0, st, a, sa, w, \
+  hipLaunchKernelGGL((gemm_blockscaled_decode_kernel<MT, KBM, TS>), grid, dim3(256), 0, st, a, sa, w, \
                      sw, c, ws, m, N, K, p.kb_per, p.splits)
 #define FP8BS_DEC_KB(MT)                      \
   if (p.kb_per <= 4) FP8BS_DEC(MT, 4);        \
@@ -819,14 +840,14 @@ int launch_decode(const uint8_t* a, const float* sa, const uint8_t* w, const flo
 #define FP8BS_GEMM_TILE 0
 #endif
 
-template <int BN, int BM, int WN, int WM, int STAGES, int WPE, bool HW>
+template <int BN, int BM, int WN, int WM, int STAGES, int WPE, int MODE>
 int launch_tiled(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c,
                  int64_t M, int64_t N, int64_t K, hipStream_t st) {
   const int64_t tiles_m = (M + BM - 1) / BM;
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t grid = (tiles_m * tiles_n + 7) / 8 * 8;
   if (grid > 0x7FFFFFF0LL) return FP8BS_ERR_SHAPE;
-  hipLaunchKernelGGL((gemm_blockscaled_tiled_kernel<BN, BM, WN, WM, STAGES, WPE, HW>),
+  hipLaunchKernelGGL((gemm_blockscaled_tiled_kernel<BN, BM, WN, WM, STAGES, WPE, MODE>),
                      dim3(static_cast<unsigned>(grid)), dim3(64 * WN * WM), 0, st, a, sa, w, sw, c,
                      M, N, K, static_cast<int>(tiles_m), static_cast<int>(tiles_n));
   return FP8BS_OK;
@@ -848,7 +869,7 @@ size_t fp8_gemm_blockscaled_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 
 namespace fp8bs {
 namespace {
-template <bool HW>
+template <int MODE>
 int gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m3, const float* w_scale,
                      void* c_bf16, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
                      void* stream) {
@@ -875,9 +896,9 @@ int gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m
   // formats (with power-of-two scales the scale product is exact there too)
   if (use_decode(M)) {
     if (M <= kDecStreamMaxM)
-      rc = launch_decode_stream(a, a_scale, w, w_scale, c, M, N, K, st);
+      rc = launch_decode_stream<MODE == 2>(a, a_scale, w, w_scale, c, M, N, K, st);
     else
-      rc = launch_decode(a, a_scale, w, w_scale, c, static_cast<float*>(workspace), M, N, K, st);
+      rc = launch_decode<MODE == 2>(a, a_scale, w, w_scale, c, static_cast<float*>(workspace), M, N, K, st);
     if (rc != FP8BS_OK) return rc;
     return launch_status();
   }
@@ -886,15 +907,15 @@ int gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m
   // else 128 x 128 tiles (two workgroups per CU)
   const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles256 >= dev.num_cus)
-    rc = launch_tiled<256, 256, 2, 4, 2, 2, HW>(a, a_scale, w, w_scale, c, M, N, K, st);
+    rc = launch_tiled<256, 256, 2, 4, 2, 2, MODE>(a, a_scale, w, w_scale, c, M, N, K, st);
   else
-    rc = launch_tiled<128, 128, 2, 2, 2, 2, HW>(a, a_scale, w, w_scale, c, M, N, K, st);
+    rc = launch_tiled<128, 128, 2, 2, 2, 2, MODE>(a, a_scale, w, w_scale, c, M, N, K, st);
 #elif FP8BS_GEMM_TILE == 1
-  rc = launch_tiled<128, 128, 2, 2, 2, 2, HW>(a, a_scale, w, w_scale, c, M, N, K, st);
+  rc = launch_tiled<128, 128, 2, 2, 2, 2, MODE>(a, a_scale, w, w_scale, c, M, N, K, st);
 #elif FP8BS_GEMM_TILE == 2
-  rc = launch_tiled<256, 256, 2, 4, 2, 2, HW>(a, a_scale, w, w_scale, c, M, N, K, st);
+  rc = launch_tiled<256, 256, 2, 4, 2, 2, MODE>(a, a_scale, w, w_scale, c, M, N, K, st);
 #elif FP8BS_GEMM_TILE == 3
-  rc = launch_tiled<256, 128, 2, 2, 3, 1, HW>(a, a_scale, w, w_scale, c, M, N, K, st);
+  rc = launch_tiled<256, 128, 2, 2, 3, 1, MODE>(a, a_scale, w, w_scale, c, M, N, K, st);
 #endif
   if (rc != FP8BS_OK) return rc;
   return launch_status();
@@ -908,15 +929,22 @@ extern "C" {
 int fp8_gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m3,
                          const float* w_scale, void* c_bf16, int64_t M, int64_t N, int64_t K,
                          void* workspace, size_t workspace_bytes, void* stream) {
-  return gemm_blockscaled<false>(a_e4m3, a_scale, w_e4m3, w_scale, c_bf16, M, N, K, workspace,
-                                 workspace_bytes, stream);
+  return gemm_blockscaled<0>(a_e4m3, a_scale, w_e4m3, w_scale, c_bf16, M, N, K, workspace,
+                             workspace_bytes, stream);
 }
 
 int fp8_gemm_blockscaled_ue8m0(const void* a_e4m3, const float* a_scale, const void* w_e4m3,
                                const float* w_scale, void* c_bf16, int64_t M, int64_t N, int64_t K,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  return gemm_blockscaled<true>(a_e4m3, a_scale, w_e4m3, w_scale, c_bf16, M, N, K, workspace,
-                                workspace_bytes, stream);
+  return gemm_blockscaled<1>(a_e4m3, a_scale, w_e4m3, w_scale, c_bf16, M, N, K, workspace,
+                             workspace_bytes, stream);
+}
+
+int fp8_gemm_tensorscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m3,
+                          const float* w_scale, void* c_bf16, int64_t M, int64_t N, int64_t K,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_blockscaled<2>(a_e4m3, a_scale, w_e4m3, w_scale, c_bf16, M, N, K, workspace,
+                             workspace_bytes, stream);
 }
 
 }  // extern "C"

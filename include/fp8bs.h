@@ -181,6 +181,23 @@ int fp8_gemm_blockscaled_ue8m0(const void* a_e4m3, const float* a_scale,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * FP8 GEMM with one scale per tensor, the consumer of fp8_amax_quant_tensor
+ * (TensorRT-LLM PR "Size the per-tensor FP8 dynamic-quant amax grid to the
+ * input", section "Description": the per-tensor quantize runs ahead of the
+ * projection GEMM and hands it the quantized input and its scale):
+ *     C = bf16_rne(fl32(a_scale[0] * w_scale[0]) * sum_k A[m,k] * W[n,k])
+ * a_scale and w_scale point at ONE fp32 each, on the device (read by the
+ * kernels, so the scale written by fp8_amax_quant_tensor needs no host copy).
+ * Other arguments, layouts, workspace and errors as fp8_gemm_blockscaled.
+ * For M > 64 the matrix cores accumulate the products over all of K and the
+ * scale product is applied once per output.
+ */
+int fp8_gemm_tensorscaled(const void* a_e4m3, const float* a_scale,
+                          const void* w_e4m3, const float* w_scale,
+                          void* c_bf16, int64_t M, int64_t N, int64_t K,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Test hook: the library's own fp32 -> e4m3 rounding step (clamp to +-448,
  * round to nearest even, sign kept), applied elementwise, so that it can be
  * checked exhaustively against a reference encoder.

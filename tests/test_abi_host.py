@@ -134,3 +134,11 @@ def test_ue8m0_argument_errors(L):
     assert f(None, P, P, P, P, 4, 128, 128, None, 0, None) == ENULL
     assert f(P, P, P, P, P, 4, 100, 128, None, 0, None) == ESHAPE
     assert f(PU, P, P, P, P, 4, 128, 128, None, 0, None) == EALIGN
+
+
+def test_tensorscaled_gemm_argument_errors(L):
+    f = L.fp8_gemm_tensorscaled
+    assert f(None, P, P, P, P, 4, 128, 128, None, 0, None) == ENULL
+    assert f(P, None, P, P, P, 4, 128, 128, None, 0, None) == ENULL
+    assert f(P, P, P, P, P, 4, 100, 128, None, 0, None) == ESHAPE
+    assert f(P, P, P, P, PU, 4, 128, 128, None, 0, None) == EALIGN
