@@ -122,6 +122,15 @@ __device__ __forceinline__ int swz(int row) {
   return ((row >> 2) & 1) | (row & 2) | (((row >> 3) & 1) << 2);
 }
 
+// Position swizzle of the activation-scale chunks (8 floats per row): rows
+// r and r+4, r+8, r+12 get distinct XOR masks, so 16 consecutive rows read
+// at one block position hit distinct banks of a 32-, 64- or 128-bank view.
+// Only bits 0-3 of r matter; the copy's rows 8g + l/8 and the read's rows
+// 16j + l%16 agree on them.
+__device__ __forceinline__ int sfold(int r) {
+  return (r & 7) ^ (((r >> 3) & 1) << 1);
+}
+
 __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row, int c0) {
   const int x = swz(row);
   const uint4 lo = *reinterpret_cast<const uint4*>(base + row * 128 + ((c0 ^ x) << 4));
@@ -134,12 +143,13 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row, int c0) {
 // TN x TM = (BN/WN) x (BM/WM) = NI x NJ MFMA tiles of 16 x 16. Per K block a
 // wave issues NI*NJ MFMAs and 4*NI*NJ scale FMAs per lane.
 //
-// Operand tiles and the K block's activation scales go from global memory
-// straight into LDS (buffer loads with the LDS bit) in a ring of STAGES
-// stages. The copies of block kb+STAGES-1 go into the stage block kb-1 left;
-// they are spread over the first MFMA rows of block kb rather than issued in
-// one burst. The activation scales of a stage are laid out so that a lane's
-// NJ scales (rows 16j + lane%16 of its wave's columns) are adjacent. The
+// Operand tiles go from global memory straight into LDS (buffer loads with
+// the LDS bit) in a ring of STAGES stages. The copies of block kb+STAGES-1 go
+// into the stage block kb-1 left; they are spread over the first MFMA rows of
+// block kb rather than issued in one burst. The activation scales go to LDS
+// in chunks of 8 K blocks (double-buffered, copied with the first block of
+// each chunk): a's scales are row-major [M, K/128], so fetching a block's
+// BM scales alone would touch BM separate cache lines per K block. The
 // weight scale is one scalar load per wave and K block (a wave's TN rows sit
 // in one 128-row weight block).
 //
@@ -158,17 +168,19 @@ struct TileCfg {
   static constexpr int NJ = TM / 16;
   static constexpr int kWBytes = BN * kBK;
   static constexpr int kABytes = BM * kBK;
-  static constexpr int kSBytes = BM * 4;
-  static constexpr int kStageBytes = kWBytes + kABytes + kSBytes;
+  static constexpr int kStageBytes = kWBytes + kABytes;
   static constexpr int kWLoads = kWBytes / 1024 / kWaves;   // 1 KiB copies per wave
   static constexpr int kALoads = kABytes / 1024 / kWaves;
-  static constexpr int kSWaves = BM / 64;                   // waves copying 64 scales each
+  // activation scales: chunks of kSChunk K blocks (BM rows x kSChunk floats),
+  // copied 4 bytes a lane, kSCopies copies per wave per chunk
+  static constexpr int kSChunk = 8;
+  static constexpr int kSChunkBytes = BM * kSChunk * 4;
+  static constexpr int kSCopies = kSChunkBytes / 256 / kWaves;
   static_assert(kWLoads * 1024 * kWaves == kWBytes && kALoads * 1024 * kWaves == kABytes, "loads");
-  static_assert(kSWaves <= kWaves, "scale copies");
+  static_assert(kSCopies * 256 * kWaves == kSChunkBytes, "scale copies");
   static_assert(TN <= 128 && 128 % TN == 0, "a wave's rows must sit in one weight block");
-  static_assert(NJ == 4 || NJ == 2, "scale vector width");
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
-  static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS");
+  static_assert(STAGES * kStageBytes + 2 * kSChunkBytes <= 160 * 1024, "LDS");
 };
 
 // MODE 0: fp32 block scales, one scale FMA per output and K block.
@@ -186,7 +198,8 @@ void gemm_blockscaled_tiled_kernel(
   constexpr int NI = T::NI, NJ = T::NJ;
   constexpr bool HW = MODE >= 1;
   constexpr bool TS = MODE == 2;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * T::kStageBytes];
+  // the operand ring, then (block scales only) two buffers of activation-scale chunks
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * T::kStageBytes + (TS ? 0 : 2 * T::kSChunkBytes)];
 
   // XCD-aware tile order: the 8 XCDs take workgroups round-robin, so give
   // each XCD one contiguous range of tiles, walked kGroupM m tiles per n tile
@@ -229,16 +242,20 @@ void gemm_blockscaled_tiled_kernel(
   const uint8_t* wtile = W + n0 * K;
   const uint8_t* atile = A + m0 * K;
   const float* stile = sa + m0 * KB;
-  // scale slot s = wave*64 + lane (first kSWaves waves) holds the scale of
-  // row wq*TM + 16*j + l16, where s = wq*TM + l16*NJ + j
-  const bool loads_scales = !TS && wave < T::kSWaves;
-  uint32_t soff;
-  {
-    const int s = wave * 64 + lane;
-    const int wq = s / T::TM, rem = s % T::TM;
-    const int row = wq * T::TM + 16 * (rem % NJ) + rem / NJ;
-    soff = static_cast<uint32_t>(row * KB * 4);
-  }
+  // Activation scales of chunk c (K blocks 8c .. 8c+7): copy q of this wave
+  // has lane l fetch row r = 8*(wave*kSCopies + q) + l/8, block
+  // 8c + ((l%8) ^ sfold(r)). Eight lanes share one row's 32 contiguous bytes,
+  // so a copy touches 8 rows' lines (a copy per K block would touch one line
+  // per row). In LDS a chunk holds 8 floats a row, block x of row r at
+  // position x ^ sfold(r): the 16 rows a K block's scale read covers then
+  // fall on distinct banks (the unswizzled stride of 8 floats conflicted).
+  // Blocks past K/128 in the last chunk read the next row's scales or zeros
+  // (past the buffer) and are never used.
+  // (kSCopies is even, so copy q's rows have bit 3 equal to q's parity)
+  static_assert(T::kSCopies % 2 == 0, "scale copies per wave");
+  const uint32_t srow = static_cast<uint32_t>((wave * T::kSCopies * 8 + (lane >> 3)) * KB * 4);
+  const uint32_t soff[2] = {srow + static_cast<uint32_t>(((lane & 7) ^ sfold(lane >> 3)) * 4),
+                            srow + static_cast<uint32_t>(((lane & 7) ^ sfold(8 + (lane >> 3))) * 4)};
   // wave-uniform: the weight-scale row address stays in scalar registers
   const int64_t nb = min<int64_t>((n0 + wn * T::TN) / 128, N / 128 - 1);
   const float* swrow = sw + nb * KB;
@@ -259,9 +276,16 @@ void gemm_blockscaled_tiled_kernel(
       copy16_buf_to_lds(aoff[q], make_rsrc(atile + cb, static_cast<uint32_t>(arows * K) - cb),
                         st + T::kWBytes + (wave * T::kALoads + q) * 1024);
     }
-    if (p == 0 && loads_scales)
-      copy4_buf_to_lds(soff, make_rsrc(stile + kb, static_cast<uint32_t>(arows * KB * 4) - 4u * kb),
-                       st + T::kWBytes + T::kABytes + wave * 256);
+    if constexpr (!TS) {
+      if (p == 0 && (kb & (T::kSChunk - 1)) == 0) {
+        const int c = kb / T::kSChunk;
+        const v4i_rsrc sr = make_rsrc(stile + c * T::kSChunk, static_cast<uint32_t>(arows * KB * 4 - c * T::kSChunk * 4));
+        const uint32_t sd = lds0 + STAGES * T::kStageBytes + (c & 1) * T::kSChunkBytes + wave * T::kSCopies * 256;
+#pragma unroll
+        for (int q = 0; q < T::kSCopies; ++q)
+          copy4_buf_to_lds(soff[q & 1] + static_cast<uint32_t>(q * 8 * KB * 4), sr, sd + q * 256);
+      }
+    }
   };
   auto issue = [&](int kb) {
 #pragma unroll
@@ -280,7 +304,7 @@ void gemm_blockscaled_tiled_kernel(
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < KB) issue(s);
-  constexpr int kPer = T::kWLoads + T::kALoads;   // copies per block, scale copy aside
+  constexpr int kPer = T::kWLoads + T::kALoads;   // operand copies per block (scale chunks aside)
   // The weight scale of block kb+1 is loaded (scalar load) after the last
   // fragment read of block kb and waited for right after the next barrier,
   // before the first fragment read: scalar loads complete out of order, so
@@ -317,18 +341,17 @@ void gemm_blockscaled_tiled_kernel(
   // of the loop body.
   auto step = [&](int kb, auto pf) {
     constexpr bool PF = decltype(pf)::value;
-    // this wave's copies of block kb are done once at most the groups of the
-    // blocks issued after it remain: STAGES-2 of them while blocks are being
-    // prefetched, fewer in the last iterations
+    // this wave's copies of block kb (and of the scale chunk that starts at
+    // kb) are done once at most the copies of the blocks issued after it
+    // remain: STAGES-2 groups of at least kPer copies while blocks are being
+    // prefetched, fewer in the last iterations (loads complete in order)
     const int ahead = PF ? STAGES - 2 : min(KB - 1 - kb, STAGES - 2);
     if (ahead <= 0) {
       wait_vmcnt<0>();
     } else if (ahead == 1) {
-      if (loads_scales) wait_vmcnt<kPer + 1>();
-      else wait_vmcnt<kPer>();
+      wait_vmcnt<kPer>();
     } else {
-      if (loads_scales) wait_vmcnt<2 * (kPer + 1)>();
-      else wait_vmcnt<2 * kPer>();
+      wait_vmcnt<2 * kPer>();
     }
     // The last W fragment of block kb-1 (wlast) was read but not yet used:
     // wait for every LDS read (and the scalar load of the weight scale) so
@@ -343,18 +366,18 @@ void gemm_blockscaled_tiled_kernel(
 
     const uint8_t* st = lds + (kb % STAGES) * T::kStageBytes;
     const uint8_t* sA = st + T::kWBytes;
-    const float* sv = reinterpret_cast<const float*>(st + T::kWBytes + T::kABytes) + wm * T::TM + (lane & 15) * NJ;
     float sav[NJ];
     if constexpr (TS) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) sav[j] = 1.0f;
-      (void)sv;
-    } else if constexpr (NJ == 4) {
-      const float4 v = *reinterpret_cast<const float4*>(sv);
-      sav[0] = v.x; sav[1] = v.y; sav[2] = v.z; sav[3] = v.w;
     } else {
-      const float2 v = *reinterpret_cast<const float2*>(sv);
-      sav[0] = v.x; sav[1] = v.y;
+      // rows wm*TM + 16j + lane%16 of the chunk holding block kb (the
+      // position swizzle depends on the row mod 16 only)
+      const float* sv = reinterpret_cast<const float*>(lds + STAGES * T::kStageBytes +
+                                                       ((kb / T::kSChunk) & 1) * T::kSChunkBytes) +
+                        (wm * T::TM + (lane & 15)) * T::kSChunk + ((kb & (T::kSChunk - 1)) ^ sfold(lane & 15));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) sav[j] = sv[j * 16 * T::kSChunk];
     }
     v8i wcur = lds_frag(st, wrow, c0);
     if constexpr (HW) {

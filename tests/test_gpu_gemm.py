@@ -74,6 +74,18 @@ def test_c4_prefill_sampled_rows():
     check_rows(qa, sa, qw, sw, rows, "C4 4096x4096x7168")
 
 
+def test_large_tiles_ragged_k_blocks_sampled_rows():
+    # enough 256 x 256 tiles to fill the chip, ragged M, and 13 K blocks: the
+    # activation scales travel in chunks of 8 K blocks, the second one partial
+    M, N, K = 4133, 4096, 1664
+    rng = np.random.default_rng(4133)
+    a = synth.f64_to_bf16_bits(rng.standard_normal((M, K)) * 2)
+    w = synth.f64_to_bf16_bits(rng.standard_normal((N, K)) * 0.02)
+    qa, sa, qw, sw = operands(a, w)
+    rows = np.unique(np.concatenate([rng.choice(M, 96, replace=False), [0, 255, 256, 4095, 4096, 4132]]))
+    check_rows(qa, sa, qw, sw, rows, f"{M}x{N}x{K}")
+
+
 def test_c5_large_m_sampled_rows():
     d = synth.gen_c5()
     qa, sa, qw, sw = operands(d["a"], d["w"], d["w_scale"])
@@ -86,7 +98,8 @@ def test_c5_large_m_sampled_rows():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (17, 256, 384), (129, 384, 256),
-                                   (200, 128, 1024), (255, 512, 128), (300, 640, 640)])
+                                   (200, 128, 1024), (255, 512, 128), (300, 640, 640),
+                                   (300, 384, 2432), (133, 256, 1152)])
 def test_ragged_shapes(M, N, K):
     rng = np.random.default_rng(M + N + K)
     a = synth.f64_to_bf16_bits(rng.standard_t(3.0, size=(M, K)))

@@ -104,7 +104,8 @@ def check(qa, sa, qw, sw, label, rows=None):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 2048, 7168), (32, 512, 512), (64, 256, 2048),
-                                   (96, 256, 512), (300, 384, 1024), (520, 640, 4096)])
+                                   (96, 256, 512), (300, 384, 1024), (520, 640, 4096),
+                                   (300, 384, 2432)])
 def test_gemm_shapes(M, N, K):
     rng = np.random.default_rng(M + 3 * N + K)
     a = synth.f64_to_bf16_bits(rng.standard_normal((M, K)) * 3)
@@ -116,6 +117,16 @@ def test_gemm_prefill_sampled_rows():
     d = synth.gen_c4()
     rows = np.random.default_rng(3).choice(4096, 48, replace=False)
     check(*operands(d["a"], d["w"]), "C4 shape", rows=rows)
+
+
+def test_gemm_large_tiles_ragged_k_blocks_sampled_rows():
+    # 256 x 256 tiles, ragged M, 13 K blocks (activation-scale chunks of 8)
+    M, N, K = 4133, 4096, 1664
+    rng = np.random.default_rng(1664)
+    a = synth.f64_to_bf16_bits(rng.standard_normal((M, K)) * 3)
+    w = synth.f64_to_bf16_bits(rng.standard_normal((N, K)) * 0.02)
+    rows = np.unique(np.concatenate([rng.choice(M, 40, replace=False), [0, 4095, 4096, 4132]]))
+    check(*operands(a, w), f"{M}x{N}x{K}", rows=rows)
 
 
 def test_gemm_large_m_drawn_scales_sampled_rows():
