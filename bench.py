@@ -54,6 +54,8 @@ def parse():
                    help="block scales: amax/448 (fp32) or powers of two (ue8m0: act-quant and weight quant "
                         "with power-of-two scales, GEMM with the matrix cores applying them); tensor: "
                         "one scale per tensor (per-tensor quant of A, then the per-tensor-scaled GEMM)")
+    p.add_argument("--fused", action="store_true",
+                   help="one call per step: block act-quant fused into the GEMM (fp8_act_quant_gemm_blockscaled)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=None, help="rows of the CPU oracle sample")
     return p.parse_args()
@@ -185,6 +187,23 @@ class Workload:
             wl += " (one scale per tensor: per-tensor quant of A, per-tensor-scaled GEMM)"
             self.config = {"workload": wl, "M": M, "N": N, "K": K}
             self.cpu = None
+            return
+        if args.fused:
+            if args.scale_fmt != "fp32" or w == "c5":
+                raise SystemExit("--fused takes fp32 block scales and one of c1, c3, c4")
+            wq, wsc = fb.fp8_weight_quant_block(bf16(d["w"]))
+            a_s = [a] + [a.clone() for _ in range(rot - 1)]
+            w_s = [wq] + [wq.clone() for _ in range(rot - 1)]
+            c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            fwsb = fb.fp8_act_quant_gemm_blockscaled_workspace_bytes(M, N, K)
+            fws = torch.empty((max(fwsb, 16),), dtype=torch.uint8, device=dev)
+            self.stages.append(("act_quant_gemm_blockscaled",
+                                lambda i: fb.fp8_act_quant_gemm_blockscaled(a_s[i % rot], w_s[i % rot], wsc,
+                                                                            out=c, workspace=fws),
+                                2 * M * K + N * K + 4 * (N // 128) * (K // 128) + 2 * M * N, 2 * M * N * K))
+            wl += " (block act-quant fused into the GEMM call)"
+            self.config = {"workload": wl, "M": M, "N": N, "K": K}
+            self.cpu = (w, M, K, N)
             return
         ue = args.scale_fmt == "ue8m0"
         act_q = fb.fp8_act_quant_block_ue8m0 if ue else fb.fp8_act_quant_block
@@ -372,15 +391,17 @@ def main():
     # dominant kernel: the GEMM when present (prefill: MFMA-bound; decode: HBM-bound)
     if "gemm_blockscaled" in stages:
         dominant = "gemm_blockscaled"
+    elif "act_quant_gemm_blockscaled" in stages:
+        dominant = "act_quant_gemm_blockscaled"
     else:
         dominant = wl.stages[0][0]
     roofline = None
     ds = stages[dominant]
     if per_stage is not None:
-        src = "gemm.hip" if dominant == "gemm_blockscaled" else "quant.hip"
+        src = "gemm.hip" if "gemm" in dominant else "quant.hip"
         fmt = "_ue8m0" if args.scale_fmt == "ue8m0" and dominant != "amax_quant_tensor" else ""
         traffic = load_traffic(f"{dominant}{fmt}:{args.workload}", src)
-        if dominant == "gemm_blockscaled" and 2 * wl.M * wl.N * wl.K / max(ds["algorithmic_bytes"], 1) > 625:
+        if "gemm" in dominant and 2 * wl.M * wl.N * wl.K / max(ds["algorithmic_bytes"], 1) > 625:
             roofline = {"bound": "mfma", "achieved": ds["TFLOP/s"], "peak": FP8_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": ds["TFLOP/s"] / FP8_PEAK_TFLOPS, "traffic": traffic}
         else:

@@ -40,6 +40,8 @@ __all__ = [
     "fp8_gemm_blockscaled_ue8m0",
     "fp8_act_quant_block_f32",
     "fp8_gemm_tensorscaled",
+    "fp8_act_quant_gemm_blockscaled_workspace_bytes",
+    "fp8_act_quant_gemm_blockscaled",
     "debug_encode_e4m3",
     "EXPORTED_SYMBOLS",
 ]
@@ -62,6 +64,8 @@ EXPORTED_SYMBOLS = (
     "fp8_gemm_blockscaled_ue8m0",
     "fp8_act_quant_block_f32",
     "fp8_gemm_tensorscaled",
+    "fp8_act_quant_gemm_blockscaled_workspace_bytes",
+    "fp8_act_quant_gemm_blockscaled",
     "fp8bs_debug_encode_e4m3",
 )
 
@@ -114,6 +118,10 @@ def lib() -> ctypes.CDLL:
     L.fp8_act_quant_block_f32.restype = ctypes.c_int
     L.fp8_gemm_tensorscaled.argtypes = [vp, fp, vp, fp, vp, i64, i64, i64, vp, sz, vp]
     L.fp8_gemm_tensorscaled.restype = ctypes.c_int
+    L.fp8_act_quant_gemm_blockscaled_workspace_bytes.argtypes = [i64, i64, i64]
+    L.fp8_act_quant_gemm_blockscaled_workspace_bytes.restype = sz
+    L.fp8_act_quant_gemm_blockscaled.argtypes = [vp, vp, fp, vp, i64, i64, i64, vp, sz, vp]
+    L.fp8_act_quant_gemm_blockscaled.restype = ctypes.c_int
     L.fp8bs_debug_encode_e4m3.argtypes = [fp, vp, i64, vp]
     L.fp8bs_debug_encode_e4m3.restype = ctypes.c_int
     _lib = L
@@ -254,6 +262,39 @@ def fp8_gemm_tensorscaled(a, a_scale, w, w_scale, out=None, workspace=None):
     """C = a_scale * w_scale * (A . W^T) (bf16 [M, N]); one fp32 scale per
     operand, as a one-element device tensor (fp8_amax_quant_tensor's output)."""
     return _gemm("fp8_gemm_tensorscaled", a, a_scale, w, w_scale, out, workspace, per_tensor=True)
+
+
+def fp8_act_quant_gemm_blockscaled_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().fp8_act_quant_gemm_blockscaled_workspace_bytes(M, N, K))
+
+
+def fp8_act_quant_gemm_blockscaled(x, w, w_scale, out=None, workspace=None):
+    """C = A_q . W^T (bf16 [M, N]) where (A_q, a_scale) is the 1x128 block
+    quantization of the bf16 activations x [M, K]; one kernel for decode
+    batches (M <= 8), else act-quant and GEMM through the workspace."""
+    _need(x, "x", torch.bfloat16)
+    if w.dtype not in (E4M3, torch.uint8):
+        raise TypeError("w must be float8_e4m3fn (or its uint8 bytes)")
+    w = _as_u8(w)
+    _need(w, "w", torch.uint8, x.device)
+    _need(w_scale, "w_scale", torch.float32, x.device)
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("x must be [M, K] and w [N, K]")
+    M, K = x.shape
+    N = w.shape[0]
+    if w_scale.shape != (N // 128, K // 128):
+        raise ValueError("w_scale must be [N/128, K/128]")
+    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    wsb = fp8_act_quant_gemm_blockscaled_workspace_bytes(M, N, K)
+    if workspace is None and wsb > 0:
+        workspace = torch.empty((wsb,), dtype=torch.uint8, device=x.device)
+    fn = "fp8_act_quant_gemm_blockscaled"
+    with torch.cuda.device(x.device):
+        rc = getattr(lib(), fn)(
+            _ptr(x), _ptr(w), _ptr(w_scale), _ptr(c), M, N, K, _ptr(workspace),
+            workspace.numel() if workspace is not None else 0, ctypes.c_void_p(_stream(x.device)))
+    _check(fn, rc)
+    return c
 
 
 def _weight_quant(fn, w: torch.Tensor, out):

@@ -92,4 +92,44 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// quantize the 8 bf16 of a uint4 with scale s (and r = 1/s on the fast path)
+template <bool kFast>
+__device__ __forceinline__ uint2 quant8(const uint4 v, float s, float r) {
+  float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = kFast ? div_by_scale(f[i], s, r) : div_ieee(f[i], s);
+  return make_uint2(pack4_e4m3(f[0], f[1], f[2], f[3]), pack4_e4m3(f[4], f[5], f[6], f[7]));
+}
+
+// One 1x128 block of bf16 held by an aligned group of 8 lanes, 16 elements
+// a lane in two uint4 (v0, v1): amax over the group, s = fl32(amax / 448),
+// the lane's 16 codes e4m3(clamp(x / s)) in o0, o1; an all-zero block gets
+// scale 0 and codes 0x00. Returns s. The quotient takes the three-operation
+// form unless some lane of the wave has a scale below kFastScaleMin (the
+// ballot keeps the choice wave-uniform); lanes outside any block must have
+// left the wave before the call.
+__device__ __forceinline__ float quant_block_bf16(const uint4 v0, const uint4 v1, uint2& o0, uint2& o1) {
+  float m = 0.0f;
+  m = absmax2(v0.x, m); m = absmax2(v0.y, m); m = absmax2(v0.z, m); m = absmax2(v0.w, m);
+  m = absmax2(v1.x, m); m = absmax2(v1.y, m); m = absmax2(v1.z, m); m = absmax2(v1.w, m);
+  const float amax = group8_max(m);
+  float s = div_ieee(amax, kE4m3Max);
+  const bool fast = s >= kFastScaleMin;
+  if (__builtin_expect(__ballot(!fast) == 0, 1)) {
+    const float r = div_ieee(1.0f, s);
+    o0 = quant8<true>(v0, s, r);
+    o1 = quant8<true>(v1, s, r);
+  } else {
+    o0 = quant8<false>(v0, s, 0.0f);
+    o1 = quant8<false>(v1, s, 0.0f);
+  }
+  if (amax == 0.0f) {
+    s = 0.0f;
+    o0 = make_uint2(0u, 0u);
+    o1 = make_uint2(0u, 0u);
+  }
+  return s;
+}
+
 }  // namespace fp8bs

@@ -667,6 +667,153 @@ int launch_decode_stream(const uint8_t* a, const float* sa, const uint8_t* w, co
 }
 
 // ---------------------------------------------------------------------------
+// Block act-quant fused into the small-M decode GEMM: C = A_q . W^T with
+// (A_q, sa) = the 1x128 block quantization of the bf16 activations X, in one
+// launch (the quantized activations never go to global memory). Same
+// workgroup shape and K order as the streaming kernel above: 16 W rows per
+// workgroup over the whole of K, wave w taking K blocks w, w+16, ... Each
+// workgroup first issues its waves' first W loads, then quantizes all of X
+// (M x K) into LDS with the act-quant kernel's rule and lane mapping (eight
+// lanes per 1x128 block, the same helper), then runs the K loop with A
+// fragments and scales read from LDS. The arithmetic after quantization is
+// the streaming kernel's, operation for operation, so the result equals the
+// two-launch path's bit for bit. Every workgroup quantizes all of X: the
+// redundant work grows with M, so this kernel serves the smallest M only
+// (kFusedMaxM).
+//
+// LDS: the wave partial sums (16 KiB), the scales [M][K/128], then the codes
+// of K block kb at kb*128*M: half h (16 bytes) of quarter q (32 bytes) of
+// row m at ((h*4 + q)*M + m)*16, so that a fragment read (lanes 16q..16q+15
+// on rows 0..15, one half) is one contiguous run of 16-byte chunks.
+// ---------------------------------------------------------------------------
+constexpr int kFusedLdsBytes = 160 * 1024;
+constexpr int kFusedRedBytes = kDecWaves * 64 * 16;
+// largest M for the one-kernel path: above it the two launches are faster
+// (measured at N = 2048, K = 7168: one kernel 6.5 / 8.6 / 10.5 us at
+// M = 1 / 4 / 8 against 9.4 / 10.4 / 11.3 us, but 12.7 against 12.2 us at
+// M = 12)
+constexpr int64_t kFusedMaxM = 8;
+
+__host__ __device__ inline int64_t fused_scale_bytes(int64_t M, int64_t K) { return (M * (K / kBK) * 4 + 15) / 16 * 16; }
+inline bool fused_fits(int64_t M, int64_t K) {
+  return M <= kFusedMaxM && kFusedRedBytes + fused_scale_bytes(M, K) + M * K <= kFusedLdsBytes;
+}
+
+template <int kDepth>
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(kDecWaves / 4, kDecWaves / 4)))
+void gemm_act_quant_decode_kernel(const uint16_t* __restrict__ X, const uint8_t* __restrict__ W,
+                                  const float* __restrict__ sw, uint16_t* __restrict__ C, int M, int64_t N,
+                                  int64_t K) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kFusedLdsBytes];
+  float4* red = reinterpret_cast<float4*>(lds);
+  const int KB = static_cast<int>(K / kBK);
+  float* ssa = reinterpret_cast<float*>(lds + kFusedRedBytes);
+  uint8_t* scode = lds + kFusedRedBytes + fused_scale_bytes(M, K);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+
+  const uint8_t* wp = W + (n0 + (lane & 15)) * K + 32 * (lane >> 4);
+  const float* swrow = sw + (n0 / 128) * KB;
+  const int nt = KB > wave ? (KB - wave + kDecWaves - 1) / kDecWaves : 0;
+  uint4 wq[kDepth][2];
+  auto loadw = [&](int d, int t) {
+    const int64_t kb = wave + static_cast<int64_t>(kDecWaves) * t;
+    wq[d][0] = *reinterpret_cast<const uint4*>(wp + kb * kBK);
+    wq[d][1] = *reinterpret_cast<const uint4*>(wp + kb * kBK + 16);
+  };
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d)
+    if (d < nt) loadw(d, d);
+
+  // quantize X (row-major M x K, block b = m*KB + kb at element 128*b);
+  // the loads of kQPass passes are issued before any of them is used
+  {
+    constexpr int kQPass = 4;
+    constexpr int kBlocksPerPass = 64 * kDecWaves / 8;
+    const int nblk = M * KB;
+    const int sub = threadIdx.x & 7;
+    for (int b0 = static_cast<int>(threadIdx.x >> 3); b0 < nblk; b0 += kQPass * kBlocksPerPass) {
+      uint4 v[kQPass][2];
+#pragma unroll
+      for (int u = 0; u < kQPass; ++u) {
+        const int b = b0 + u * kBlocksPerPass;
+        if (b < nblk) {
+          const uint4* xb = reinterpret_cast<const uint4*>(X + static_cast<int64_t>(b) * kBK);
+          v[u][0] = xb[sub];
+          v[u][1] = xb[8 + sub];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kQPass; ++u) {
+        const int b = b0 + u * kBlocksPerPass;
+        if (b < nblk) {
+          uint2 o0, o1;
+          const float sb = quant_block_bf16(v[u][0], v[u][1], o0, o1);
+          const int m = b / KB, kb = b % KB;
+          // codes of elements 8*sub.. (quarter sub/4) and 64 + 8*sub..
+          // (quarter 2 + sub/4); both at byte 8*(sub%4) of their quarter
+          const int h = (sub & 3) >> 1;
+          uint8_t* cb = scode + static_cast<int64_t>(kb) * kBK * M + (sub & 1) * 8;
+          *reinterpret_cast<uint2*>(cb + ((h * 4 + (sub >> 2)) * M + m) * 16) = o0;
+          *reinterpret_cast<uint2*>(cb + ((h * 4 + 2 + (sub >> 2)) * M + m) * 16) = o1;
+          if (sub == 0) ssa[b] = sb;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // lane l: A row min(l%16, M-1) (rows past M repeat row M-1; their outputs
+  // are never stored), quarter l/16 of each K block
+  const int ar = min(lane & 15, M - 1);
+  const uint8_t* ap = scode + ((lane >> 4) * M + ar) * 16;
+  const float* sp = ssa + ar * KB;
+  v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t0 = 0; t0 < nt; t0 += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int t = t0 + d;
+      if (t < nt) {
+        const int kb = wave + kDecWaves * t;
+        const v8i wf = v8i{(int)wq[d][0].x, (int)wq[d][0].y, (int)wq[d][0].z, (int)wq[d][0].w,
+                           (int)wq[d][1].x, (int)wq[d][1].y, (int)wq[d][1].z, (int)wq[d][1].w};
+        const uint8_t* ak = ap + static_cast<int64_t>(kb) * kBK * M;
+        const uint4 lo = *reinterpret_cast<const uint4*>(ak);
+        const uint4 hi = *reinterpret_cast<const uint4*>(ak + 4 * M * 16);
+        const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const float cs = sp[kb] * swrow[kb];
+        if (t + kDepth < nt) loadw(d, t + kDepth);
+        const v4f p = mfma_16x16x128_fp8(wf, af);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(p[r], cs, acc[r]);
+      }
+    }
+  }
+
+  // the waves' partial sums, added in wave order (as in the streaming kernel)
+  red[wave * 64 + lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < 64) {
+    const int m = t & 15;
+    if (m < M) {
+      float4 sum = red[t];
+#pragma unroll
+      for (int w = 1; w < kDecWaves; ++w) {
+        const float4 v = red[w * 64 + t];
+        sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+      }
+      const int64_t n = n0 + 4 * (t >> 4);
+      uint2 o;
+      o.x = bf16x2_rne(sum.x, sum.y);
+      o.y = bf16x2_rne(sum.z, sum.w);
+      *reinterpret_cast<uint2*>(C + m * N + n) = o;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Larger decode M (16 < M <= 64): the work is cut into many pieces of W so
 // that A is shared: workgroup (n tile of 64 rows, K split)
 // has four waves, wave w owning W rows 16w..16w+15 of the tile. Each wave
@@ -968,6 +1115,57 @@ int fp8_gemm_tensorscaled(const void* a_e4m3, const float* a_scale, const void* 
                           void* workspace, size_t workspace_bytes, void* stream) {
   return gemm_blockscaled<2>(a_e4m3, a_scale, w_e4m3, w_scale, c_bf16, M, N, K, workspace,
                              workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace fp8bs {
+namespace {
+inline int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+inline bool act_gemm_shape_ok(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return false;
+  if (M > (INT64_MAX / K) || M > (INT64_MAX / N) || N > (INT64_MAX / K)) return false;
+  return K <= (int64_t{1} << 22);
+}
+}  // namespace
+}  // namespace fp8bs
+
+extern "C" {
+
+size_t fp8_act_quant_gemm_blockscaled_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (!act_gemm_shape_ok(M, N, K) || fused_fits(M, K)) return 0;
+  return static_cast<size_t>(round256(M * K) + round256(M * (K / kBK) * 4)) +
+         fp8_gemm_blockscaled_workspace_bytes(M, N, K);
+}
+
+int fp8_act_quant_gemm_blockscaled(const void* x_bf16, const void* w_e4m3, const float* w_scale, void* c_bf16,
+                                   int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (!x_bf16 || !w_e4m3 || !w_scale || !c_bf16) return FP8BS_ERR_NULL;
+  if (!act_gemm_shape_ok(M, N, K)) return FP8BS_ERR_SHAPE;
+  if (!aligned(x_bf16, 16) || !aligned(w_e4m3, 16) || !aligned(c_bf16, 16) || !aligned(w_scale, 4))
+    return FP8BS_ERR_ALIGN;
+  if (fused_fits(M, K)) {
+    const DeviceInfo dev = current_device();
+    if (dev.status != FP8BS_OK) return dev.status;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((gemm_act_quant_decode_kernel<4>), dim3(static_cast<unsigned>(N / 16)),
+                       dim3(64 * kDecWaves), 0, as_stream(stream), static_cast<const uint16_t*>(x_bf16),
+                       static_cast<const uint8_t*>(w_e4m3), w_scale, static_cast<uint16_t*>(c_bf16),
+                       static_cast<int>(M), N, K);
+    return launch_status();
+  }
+  // two launches through the workspace: block act-quant, then the GEMM
+  const size_t need = fp8_act_quant_gemm_blockscaled_workspace_bytes(M, N, K);
+  if (!workspace || workspace_bytes < need) return FP8BS_ERR_WORKSPACE;
+  uint8_t* q = static_cast<uint8_t*>(workspace);
+  float* sa = reinterpret_cast<float*>(q + round256(M * K));
+  uint8_t* gws = q + round256(M * K) + round256(M * (K / kBK) * 4);
+  const size_t gws_bytes = need - static_cast<size_t>(gws - q);
+  int rc = fp8_act_quant_block(x_bf16, M, K, q, sa, stream);
+  if (rc != FP8BS_OK) return rc;
+  return fp8_gemm_blockscaled(q, sa, w_e4m3, w_scale, c_bf16, M, N, K, gws_bytes ? gws : nullptr, gws_bytes,
+                              stream);
 }
 
 }  // extern "C"

@@ -27,16 +27,6 @@ constexpr int kThreads = 256;
 // block amax is a 3-step DPP max inside the 8-lane group.
 // ---------------------------------------------------------------------------
 
-// quantize the 8 bf16 of a uint4 with scale s (and r = 1/s on the fast path)
-template <bool kFast>
-__device__ __forceinline__ uint2 quant8(const uint4 v, float s, float r) {
-  float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = kFast ? div_by_scale(f[i], s, r) : div_ieee(f[i], s);
-  return make_uint2(pack4_e4m3(f[0], f[1], f[2], f[3]), pack4_e4m3(f[4], f[5], f[6], f[7]));
-}
-
 // Power-of-two scale (the ue8m0 variants): the smallest 2^e >= amax/448 with
 // e >= -127, read off amax's bits (amax > 0). With amax = m * 2^E, m in [1, 2)
 // and 448 = 1.75 * 2^8: e = E - 8 if m <= 1.75, else E - 7; subnormal amax
@@ -72,34 +62,24 @@ __global__ __launch_bounds__(kThreads) void act_quant_block_kernel(
   const uint4 v0 = x[blk * 16 + sub];
   const uint4 v1 = x[blk * 16 + 8 + sub];
 
-  float m = 0.0f;
-  m = absmax2(v0.x, m); m = absmax2(v0.y, m); m = absmax2(v0.z, m); m = absmax2(v0.w, m);
-  m = absmax2(v1.x, m); m = absmax2(v1.y, m); m = absmax2(v1.z, m); m = absmax2(v1.w, m);
-  const float amax = group8_max(m);
-
   float s;
   uint2 o0, o1;
   if constexpr (P2) {
+    float m = 0.0f;
+    m = absmax2(v0.x, m); m = absmax2(v0.y, m); m = absmax2(v0.z, m); m = absmax2(v0.w, m);
+    m = absmax2(v1.x, m); m = absmax2(v1.y, m); m = absmax2(v1.z, m); m = absmax2(v1.w, m);
+    const float amax = group8_max(m);
     float r;
     pow2_scale(amax, s, r);
     o0 = quant8_pow2(v0, r);
     o1 = quant8_pow2(v1, r);
-  } else {
-    s = div_ieee(amax, kE4m3Max);
-    const bool fast = s >= kFastScaleMin;
-    if (__builtin_expect(__ballot(!fast) == 0, 1)) {
-      const float r = div_ieee(1.0f, s);
-      o0 = quant8<true>(v0, s, r);
-      o1 = quant8<true>(v1, s, r);
-    } else {
-      o0 = quant8<false>(v0, s, 0.0f);
-      o1 = quant8<false>(v1, s, 0.0f);
+    if (amax == 0.0f) {  // all-zero block: scale 0, codes 0x00
+      s = 0.0f;
+      o0 = make_uint2(0u, 0u);
+      o1 = make_uint2(0u, 0u);
     }
-  }
-  if (amax == 0.0f) {  // all-zero block: scale 0, codes 0x00
-    s = 0.0f;
-    o0 = make_uint2(0u, 0u);
-    o1 = make_uint2(0u, 0u);
+  } else {
+    s = quant_block_bf16(v0, v1, o0, o1);
   }
   q[blk * 16 + sub] = o0;
   q[blk * 16 + 8 + sub] = o1;

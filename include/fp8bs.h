@@ -198,6 +198,32 @@ int fp8_gemm_tensorscaled(const void* a_e4m3, const float* a_scale,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Block act-quant and block-scaled GEMM in one call, for decode batches:
+ *     (A_q, a_scale) = the 1x128 block quantization of x (fp8_act_quant_block)
+ *     C = fp8_gemm_blockscaled(A_q, a_scale, w_e4m3, w_scale)
+ * The DeepSeek-V3 page ("How to Profile DeepSeek-V3 Inference Kernels Using
+ * Triton Autotuning", section "Analyzing FP8 Quantization Sensitivity" and
+ * the FAQ entry on profiling act_quant_kernel separately) notes that the
+ * activation quantization can dominate at small batch sizes. For M <= 8
+ * (and M*K + M*K/32 <= 144 KiB, e.g. K <= 17792 at M = 8) this is ONE kernel:
+ * every workgroup quantizes x into LDS and runs the decode GEMM from there,
+ * with no workspace and no quantized copy of x in global memory; C is then
+ * bit-for-bit the two-call result. Otherwise the call enqueues the two steps
+ * through the workspace (codes, scales, then the GEMM's own workspace).
+ *
+ *   x_bf16   [M, K] bf16, 16-byte aligned           (input)
+ *   w_e4m3, w_scale, c_bf16: as fp8_gemm_blockscaled
+ *   workspace  at least fp8_act_quant_gemm_blockscaled_workspace_bytes(M, N, K)
+ *              bytes, 16-byte aligned (NULL allowed when that size is 0);
+ *              not to be shared by calls that can run concurrently
+ * Requires the shapes of fp8_gemm_blockscaled. Errors as above.
+ */
+size_t fp8_act_quant_gemm_blockscaled_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int fp8_act_quant_gemm_blockscaled(const void* x_bf16, const void* w_e4m3, const float* w_scale,
+                                   void* c_bf16, int64_t M, int64_t N, int64_t K,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Test hook: the library's own fp32 -> e4m3 rounding step (clamp to +-448,
  * round to nearest even, sign kept), applied elementwise, so that it can be
  * checked exhaustively against a reference encoder.

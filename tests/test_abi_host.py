@@ -142,3 +142,24 @@ def test_tensorscaled_gemm_argument_errors(L):
     assert f(P, None, P, P, P, 4, 128, 128, None, 0, None) == ENULL
     assert f(P, P, P, P, P, 4, 100, 128, None, 0, None) == ESHAPE
     assert f(P, P, P, P, PU, 4, 128, 128, None, 0, None) == EALIGN
+
+
+def test_act_quant_gemm_argument_errors(L):
+    f = L.fp8_act_quant_gemm_blockscaled
+    ws = L.fp8_act_quant_gemm_blockscaled_workspace_bytes
+    assert f(None, P, P, P, 4, 128, 128, None, 0, None) == ENULL
+    assert f(P, P, None, P, 4, 128, 128, None, 0, None) == ENULL
+    assert f(P, P, P, P, 0, 128, 128, None, 0, None) == ESHAPE
+    assert f(P, P, P, P, 4, 100, 128, None, 0, None) == ESHAPE
+    assert f(P, P, P, P, 4, 128, 130, None, 0, None) == ESHAPE
+    assert f(PU, P, P, P, 4, 128, 128, None, 0, None) == EALIGN
+    assert f(P, P, P, PU, 4, 128, 128, None, 0, None) == EALIGN
+    # one kernel (no workspace) for M <= 8 while x's codes and scales fit in LDS
+    assert ws(1, 2048, 7168) == 0 and ws(8, 2048, 7168) == 0 and ws(8, 2048, 17792) == 0
+    # otherwise act-quant and GEMM through the workspace: codes, scales, GEMM workspace
+    assert ws(8, 2048, 17920) == 8 * 17920 + 4608
+    assert ws(16, 2048, 7168) == 16 * 7168 + 3584
+    assert ws(64, 2048, 7168) == 64 * 7168 + 14336 + L.fp8_gemm_blockscaled_workspace_bytes(64, 2048, 7168)
+    assert ws(4096, 4096, 7168) == 4096 * 7168 + 4096 * 56 * 4
+    assert f(P, P, P, P, 17, 128, 128, None, 0, None) == EWS
+    assert f(P, P, P, P, 17, 128, 128, P, ws(17, 128, 128) - 1, None) == EWS
