@@ -667,19 +667,26 @@ int launch_decode_stream(const uint8_t* a, const float* sa, const uint8_t* w, co
 }
 
 // ---------------------------------------------------------------------------
-// Block act-quant fused into the small-M decode GEMM: C = A_q . W^T with
-// (A_q, sa) = the 1x128 block quantization of the bf16 activations X, in one
-// launch (the quantized activations never go to global memory). Same
-// workgroup shape and K order as the streaming kernel above: 16 W rows per
-// workgroup over the whole of K, wave w taking K blocks w, w+16, ... Each
-// workgroup first issues its waves' first W loads, then quantizes all of X
-// (M x K) into LDS with the act-quant kernel's rule and lane mapping (eight
-// lanes per 1x128 block, the same helper), then runs the K loop with A
-// fragments and scales read from LDS. The arithmetic after quantization is
-// the streaming kernel's, operation for operation, so the result equals the
-// two-launch path's bit for bit. Every workgroup quantizes all of X: the
-// redundant work grows with M, so this kernel serves the smallest M only
-// (kFusedMaxM).
+// Small-M decode GEMM with the activations in LDS (M <= kDecLdsMaxM), and
+// the same kernel with the block act-quant fused in (M <= kFusedMaxM).
+//
+// Same workgroup shape and K order as the streaming kernel above: 16 W rows
+// per workgroup over the whole of K, wave w taking K blocks w, w+16, ...
+// Each workgroup first issues its waves' first W loads, then stages all of A
+// (M x K codes and the M x K/128 scales) in LDS while those loads are in
+// flight, and runs the K loop with A fragments and scales read from LDS: the
+// A loads of the streaming kernel go through L1 and L2 once per K block and
+// wave and their latency adds to every block's (measured at N = 2048,
+// K = 7168: 10.6 us at M = 16 with them, 6.0 us with A not loaded at all).
+//
+// QUANT: C = A_q . W^T with (A_q, sa) the 1x128 block quantization of the
+// bf16 activations X, in one launch (the quantized activations never go to
+// global memory): the staging step quantizes X with the act-quant kernel's
+// rule and lane mapping (eight lanes per 1x128 block, the same helper).
+// The arithmetic after staging is the streaming kernel's, operation for
+// operation, so the results are those of the two-launch path bit for bit.
+// Every workgroup quantizes all of X: that redundant work grows with M, so
+// the fused form serves the smallest M only (kFusedMaxM).
 //
 // LDS: the wave partial sums (16 KiB), the scales [M][K/128], then the codes
 // of K block kb at kb*128*M: half h (16 bytes) of quarter q (32 bytes) of
@@ -688,22 +695,31 @@ int launch_decode_stream(const uint8_t* a, const float* sa, const uint8_t* w, co
 // ---------------------------------------------------------------------------
 constexpr int kFusedLdsBytes = 160 * 1024;
 constexpr int kFusedRedBytes = kDecWaves * 64 * 16;
-// largest M for the one-kernel path: above it the two launches are faster
-// (measured at N = 2048, K = 7168: one kernel 6.5 / 8.6 / 10.5 us at
-// M = 1 / 4 / 8 against 9.4 / 10.4 / 11.3 us, but 12.7 against 12.2 us at
-// M = 12)
+// largest M for the one-kernel act-quant + GEMM: above it the two launches
+// are faster (measured at N = 2048, K = 7168: one kernel 6.5 / 8.6 / 10.5 us
+// at M = 1 / 4 / 8 against 9.4 / 10.4 / 11.3 us, but 12.7 against 12.2 us
+// at M = 12)
 constexpr int64_t kFusedMaxM = 8;
 
 __host__ __device__ inline int64_t fused_scale_bytes(int64_t M, int64_t K) { return (M * (K / kBK) * 4 + 15) / 16 * 16; }
-inline bool fused_fits(int64_t M, int64_t K) {
-  return M <= kFusedMaxM && kFusedRedBytes + fused_scale_bytes(M, K) + M * K <= kFusedLdsBytes;
+// largest M for which the GEMM alone stages A in LDS: the staging step runs
+// before the K loop and grows with M, the per-block A loads it saves cost
+// less from M = 4 on (N = 2048, K = 7168: 6.2 against 6.9 us at M = 1, 7.9
+// against 7.8 us at M = 4, 12.8 against 10.6 us at M = 16)
+constexpr int64_t kDecLdsMaxM = 2;
+inline bool lds_fits(int64_t M, int64_t K) {
+  return kFusedRedBytes + fused_scale_bytes(M, K) + M * K <= kFusedLdsBytes;
 }
+inline bool decode_lds_fits(int64_t M, int64_t K) { return M <= kDecLdsMaxM && lds_fits(M, K); }
+inline bool fused_fits(int64_t M, int64_t K) { return M <= kFusedMaxM && lds_fits(M, K); }
 
-template <int kDepth>
+// QUANT: Xin is bf16 X [M, K] (sa unused); else Xin is e4m3 A [M, K] with
+// scales sa [M, K/128] (TS: one scale per tensor, sa[0] * sw[0])
+template <int kDepth, bool QUANT, bool TS>
 __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(kDecWaves / 4, kDecWaves / 4)))
-void gemm_act_quant_decode_kernel(const uint16_t* __restrict__ X, const uint8_t* __restrict__ W,
-                                  const float* __restrict__ sw, uint16_t* __restrict__ C, int M, int64_t N,
-                                  int64_t K) {
+void gemm_decode_lds_kernel(const void* __restrict__ Xin, const float* __restrict__ sa, const uint8_t* __restrict__ W,
+                            const float* __restrict__ sw, uint16_t* __restrict__ C, int M, int64_t N, int64_t K) {
+  static_assert(!(QUANT && TS), "the fused form takes block scales");
   __shared__ __attribute__((aligned(16))) uint8_t lds[kFusedLdsBytes];
   float4* red = reinterpret_cast<float4*>(lds);
   const int KB = static_cast<int>(K / kBK);
@@ -726,17 +742,18 @@ void gemm_act_quant_decode_kernel(const uint16_t* __restrict__ X, const uint8_t*
   for (int d = 0; d < kDepth; ++d)
     if (d < nt) loadw(d, d);
 
-  // quantize X (row-major M x K, block b = m*KB + kb at element 128*b);
-  // the loads of kQPass passes are issued before any of them is used
-  {
-    constexpr int kQPass = 4;
+  // stage A in LDS; the loads of kPass passes are issued before any is used
+  constexpr int kPass = 4;
+  if constexpr (QUANT) {
+    // quantize X (row-major M x K, block b = m*KB + kb at element 128*b)
+    const uint16_t* X = static_cast<const uint16_t*>(Xin);
     constexpr int kBlocksPerPass = 64 * kDecWaves / 8;
     const int nblk = M * KB;
     const int sub = threadIdx.x & 7;
-    for (int b0 = static_cast<int>(threadIdx.x >> 3); b0 < nblk; b0 += kQPass * kBlocksPerPass) {
-      uint4 v[kQPass][2];
+    for (int b0 = static_cast<int>(threadIdx.x >> 3); b0 < nblk; b0 += kPass * kBlocksPerPass) {
+      uint4 v[kPass][2];
 #pragma unroll
-      for (int u = 0; u < kQPass; ++u) {
+      for (int u = 0; u < kPass; ++u) {
         const int b = b0 + u * kBlocksPerPass;
         if (b < nblk) {
           const uint4* xb = reinterpret_cast<const uint4*>(X + static_cast<int64_t>(b) * kBK);
@@ -745,7 +762,7 @@ void gemm_act_quant_decode_kernel(const uint16_t* __restrict__ X, const uint8_t*
         }
       }
 #pragma unroll
-      for (int u = 0; u < kQPass; ++u) {
+      for (int u = 0; u < kPass; ++u) {
         const int b = b0 + u * kBlocksPerPass;
         if (b < nblk) {
           uint2 o0, o1;
@@ -761,6 +778,29 @@ void gemm_act_quant_decode_kernel(const uint16_t* __restrict__ X, const uint8_t*
         }
       }
     }
+  } else {
+    // copy the codes, 16 bytes a lane: chunk c = 2q + h of row m, block kb
+    const uint8_t* A = static_cast<const uint8_t*>(Xin);
+    const int nchunk = M * KB * 8;
+    for (int i0 = static_cast<int>(threadIdx.x); i0 < nchunk; i0 += kPass * 64 * kDecWaves) {
+      uint4 v[kPass];
+#pragma unroll
+      for (int u = 0; u < kPass; ++u) {
+        const int i = i0 + u * 64 * kDecWaves;
+        if (i < nchunk) v[u] = *reinterpret_cast<const uint4*>(A + static_cast<int64_t>(i) * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < kPass; ++u) {
+        const int i = i0 + u * 64 * kDecWaves;
+        if (i < nchunk) {
+          const int m = i / (KB * 8), kb = (i / 8) % KB, c = i % 8;
+          *reinterpret_cast<uint4*>(scode + static_cast<int64_t>(kb) * kBK * M +
+                                    (((c & 1) * 4 + (c >> 1)) * M + m) * 16) = v[u];
+        }
+      }
+    }
+    if constexpr (!TS)
+      for (int i = static_cast<int>(threadIdx.x); i < M * KB; i += 64 * kDecWaves) ssa[i] = sa[i];
   }
   __syncthreads();
 
@@ -769,6 +809,7 @@ void gemm_act_quant_decode_kernel(const uint16_t* __restrict__ X, const uint8_t*
   const int ar = min(lane & 15, M - 1);
   const uint8_t* ap = scode + ((lane >> 4) * M + ar) * 16;
   const float* sp = ssa + ar * KB;
+  const float cst = TS ? sa[0] * sw[0] : 0.0f;
   v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   for (int t0 = 0; t0 < nt; t0 += kDepth) {
 #pragma unroll
@@ -782,7 +823,7 @@ void gemm_act_quant_decode_kernel(const uint16_t* __restrict__ X, const uint8_t*
         const uint4 lo = *reinterpret_cast<const uint4*>(ak);
         const uint4 hi = *reinterpret_cast<const uint4*>(ak + 4 * M * 16);
         const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        const float cs = sp[kb] * swrow[kb];
+        const float cs = TS ? cst : sp[kb] * swrow[kb];
         if (t + kDepth < nt) loadw(d, t + kDepth);
         const v4f p = mfma_16x16x128_fp8(wf, af);
 #pragma unroll
@@ -811,6 +852,14 @@ void gemm_act_quant_decode_kernel(const uint16_t* __restrict__ X, const uint8_t*
       *reinterpret_cast<uint2*>(C + m * N + n) = o;
     }
   }
+}
+
+template <bool QUANT, bool TS>
+int launch_decode_lds(const void* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c, int64_t M,
+                      int64_t N, int64_t K, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_decode_lds_kernel<4, QUANT, TS>), dim3(static_cast<unsigned>(N / 16)),
+                     dim3(64 * kDecWaves), 0, st, a, sa, w, sw, c, static_cast<int>(M), N, K);
+  return FP8BS_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -1065,7 +1114,9 @@ int gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m
   // decode shapes are bound by streaming W: the FMA kernels serve both scale
   // formats (with power-of-two scales the scale product is exact there too)
   if (use_decode(M)) {
-    if (M <= kDecStreamMaxM)
+    if (decode_lds_fits(M, K))
+      rc = launch_decode_lds<false, MODE == 2>(a, a_scale, w, w_scale, c, M, N, K, st);
+    else if (M <= kDecStreamMaxM)
       rc = launch_decode_stream<MODE == 2>(a, a_scale, w, w_scale, c, M, N, K, st);
     else
       rc = launch_decode<MODE == 2>(a, a_scale, w, w_scale, c, static_cast<float*>(workspace), M, N, K, st);
@@ -1149,10 +1200,8 @@ int fp8_act_quant_gemm_blockscaled(const void* x_bf16, const void* w_e4m3, const
     const DeviceInfo dev = current_device();
     if (dev.status != FP8BS_OK) return dev.status;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((gemm_act_quant_decode_kernel<4>), dim3(static_cast<unsigned>(N / 16)),
-                       dim3(64 * kDecWaves), 0, as_stream(stream), static_cast<const uint16_t*>(x_bf16),
-                       static_cast<const uint8_t*>(w_e4m3), w_scale, static_cast<uint16_t*>(c_bf16),
-                       static_cast<int>(M), N, K);
+    launch_decode_lds<true, false>(x_bf16, nullptr, static_cast<const uint8_t*>(w_e4m3), w_scale,
+                                   static_cast<uint16_t*>(c_bf16), M, N, K, as_stream(stream));
     return launch_status();
   }
   // two launches through the workspace: block act-quant, then the GEMM

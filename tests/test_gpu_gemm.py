@@ -209,11 +209,14 @@ def test_bit_exact_against_matrix_core_model(dist):
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (5, 256, 1024), (16, 2048, 7168), (17, 384, 2048),
                                    (33, 640, 4096), (64, 2048, 7168), (64, 128, 128 * 40), (48, 7168, 2048),
-                                   (3, 256, 128 * 7), (16, 128, 128 * 600), (40, 128, 128 * 500)])
+                                   (3, 256, 128 * 7), (16, 128, 128 * 600), (40, 128, 128 * 500),
+                                   (2, 128, 71424), (2, 128, 71552)])
 def test_decode_shapes(M, N, K):
     # M <= 16: sixteen waves per 16 W rows, each taking every sixteenth K
     # block, partial sums added in wave order (K = 7 blocks leaves waves
     # without a block; K = 600 blocks runs many prefetch rounds per wave).
+    # For M <= 2 A is staged in LDS while it fits (2 x 71424 is the largest),
+    # else it is read from global memory per block (2 x 71552, M > 2).
     # 16 < M <= 64: several K splits, fp32 partials in the workspace, reduced
     # in split order.
     rng = np.random.default_rng(M * 7 + N + K)

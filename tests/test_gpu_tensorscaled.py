@@ -36,7 +36,7 @@ def tensor_operands(a_bits, w_bits):
     return qa, sa, qw, sw
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 2048, 7168), (16, 512, 1024), (64, 2048, 2048), (33, 256, 640),
+@pytest.mark.parametrize("M,N,K", [(1, 2048, 7168), (16, 512, 1024), (4, 128, 128 * 400), (64, 2048, 2048), (33, 256, 640),
                                    (96, 256, 512), (300, 384, 1024), (1000, 1024, 2048)])
 def test_shapes(M, N, K):
     rng = np.random.default_rng(M * 5 + N + K)
