@@ -56,6 +56,8 @@ def parse():
                         "one scale per tensor (per-tensor quant of A, then the per-tensor-scaled GEMM)")
     p.add_argument("--fused", action="store_true",
                    help="one call per step: block act-quant fused into the GEMM (fp8_act_quant_gemm_blockscaled)")
+    p.add_argument("--separate-quant", action="store_true",
+                   help="large-M workload: block and per-tensor quant as two calls (default: one call)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=None, help="rows of the CPU oracle sample")
     return p.parse_args()
@@ -221,10 +223,22 @@ class Workload:
         c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         gwsb = fb.fp8_gemm_blockscaled_workspace_bytes(M, N, K)
         gws = torch.empty((max(gwsb, 16),), dtype=torch.uint8, device=dev)
-        self.stages.append(("act_quant_block",
-                            lambda i: act_q(a_s[i % rot], out=(qa[i % rot], sa[i % rot])),
-                            2 * M * K + M * K + 4 * (M * K // 128), 0))
-        if w == "c5":
+        fuse_bt = w == "c5" and not ue and not args.separate_quant
+        if fuse_bt:
+            # block and per-tensor quant of A in one call (A read twice, not three times)
+            qt = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+            st = torch.empty((1,), dtype=torch.float32, device=dev)
+            bwsb = fb.fp8_act_quant_block_tensor_workspace_bytes(M, K)
+            bws = torch.zeros((max(bwsb, 16),), dtype=torch.uint8, device=dev)
+            self.stages.append(("act_quant_block_tensor",
+                                lambda i: fb.fp8_act_quant_block_tensor(
+                                    a_s[i % rot], out=(qa[i % rot], sa[i % rot], qt, st), workspace=bws),
+                                2 * M * K + 2 * M * K + 4 * (M * K // 128) + 4, 0))
+        else:
+            self.stages.append(("act_quant_block",
+                                lambda i: act_q(a_s[i % rot], out=(qa[i % rot], sa[i % rot])),
+                                2 * M * K + M * K + 4 * (M * K // 128), 0))
+        if w == "c5" and not fuse_bt:
             qt = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
             st = torch.empty((1,), dtype=torch.float32, device=dev)
             twsb = fb.fp8_amax_quant_tensor_workspace_bytes(M * K)
@@ -237,6 +251,8 @@ class Workload:
                             lambda i: gemm_f(qa[i % rot], sa[i % rot], w_s[i % rot], wsc,
                                              out=c, workspace=gws),
                             gemm_bytes, 2 * M * N * K))
+        if fuse_bt:
+            wl += " (block and per-tensor quant of A in one call)"
         if ue:
             wl += " (power-of-two block scales)"
         self.config = {"workload": wl, "M": M, "N": N, "K": K}

@@ -42,6 +42,8 @@ __all__ = [
     "fp8_gemm_tensorscaled",
     "fp8_act_quant_gemm_blockscaled_workspace_bytes",
     "fp8_act_quant_gemm_blockscaled",
+    "fp8_act_quant_block_tensor_workspace_bytes",
+    "fp8_act_quant_block_tensor",
     "debug_encode_e4m3",
     "EXPORTED_SYMBOLS",
 ]
@@ -66,6 +68,8 @@ EXPORTED_SYMBOLS = (
     "fp8_gemm_tensorscaled",
     "fp8_act_quant_gemm_blockscaled_workspace_bytes",
     "fp8_act_quant_gemm_blockscaled",
+    "fp8_act_quant_block_tensor_workspace_bytes",
+    "fp8_act_quant_block_tensor",
     "fp8bs_debug_encode_e4m3",
 )
 
@@ -122,6 +126,10 @@ def lib() -> ctypes.CDLL:
     L.fp8_act_quant_gemm_blockscaled_workspace_bytes.restype = sz
     L.fp8_act_quant_gemm_blockscaled.argtypes = [vp, vp, fp, vp, i64, i64, i64, vp, sz, vp]
     L.fp8_act_quant_gemm_blockscaled.restype = ctypes.c_int
+    L.fp8_act_quant_block_tensor_workspace_bytes.argtypes = [i64, i64]
+    L.fp8_act_quant_block_tensor_workspace_bytes.restype = sz
+    L.fp8_act_quant_block_tensor.argtypes = [vp, i64, i64, vp, fp, vp, fp, vp, sz, vp]
+    L.fp8_act_quant_block_tensor.restype = ctypes.c_int
     L.fp8bs_debug_encode_e4m3.argtypes = [fp, vp, i64, vp]
     L.fp8bs_debug_encode_e4m3.restype = ctypes.c_int
     _lib = L
@@ -207,6 +215,37 @@ def fp8_amax_quant_tensor(x: torch.Tensor, out=None, workspace=None):
             workspace.numel() if workspace is not None else 0, ctypes.c_void_p(_stream(x.device)))
     _check("fp8_amax_quant_tensor", rc)
     return q, s
+
+
+def fp8_act_quant_block_tensor_workspace_bytes(M: int, K: int) -> int:
+    return int(lib().fp8_act_quant_block_tensor_workspace_bytes(M, K))
+
+
+def fp8_act_quant_block_tensor(x: torch.Tensor, out=None, workspace=None):
+    """Block and per-tensor quantization of the same bf16 ``x`` [M, K]:
+    returns (q_block, block_scale, q_tensor, tensor_scale), bit for bit those
+    of fp8_act_quant_block and fp8_amax_quant_tensor."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    if out is None:
+        qb = torch.empty((M, K), dtype=E4M3, device=x.device)
+        sb = torch.empty((M, K // 128 if K % 128 == 0 else 1), dtype=torch.float32, device=x.device)
+        qt = torch.empty((M, K), dtype=E4M3, device=x.device)
+        st = torch.empty((1,), dtype=torch.float32, device=x.device)
+    else:
+        qb, sb, qt, st = out
+    wsb = fp8_act_quant_block_tensor_workspace_bytes(M, K)
+    if workspace is None and wsb > 0:
+        workspace = torch.empty((wsb,), dtype=torch.uint8, device=x.device)
+    fn = "fp8_act_quant_block_tensor"
+    with torch.cuda.device(x.device):
+        rc = getattr(lib(), fn)(_ptr(x), M, K, _ptr(qb), _ptr(sb), _ptr(qt), _ptr(st), _ptr(workspace),
+                                workspace.numel() if workspace is not None else 0,
+                                ctypes.c_void_p(_stream(x.device)))
+    _check(fn, rc)
+    return qb, sb, qt, st
 
 
 def fp8_gemm_blockscaled_workspace_bytes(M: int, N: int, K: int) -> int:

@@ -105,11 +105,12 @@ __device__ __forceinline__ uint2 quant8(const uint4 v, float s, float r) {
 // One 1x128 block of bf16 held by an aligned group of 8 lanes, 16 elements
 // a lane in two uint4 (v0, v1): amax over the group, s = fl32(amax / 448),
 // the lane's 16 codes e4m3(clamp(x / s)) in o0, o1; an all-zero block gets
-// scale 0 and codes 0x00. Returns s. The quotient takes the three-operation
+// scale 0 and codes 0x00. Returns s (and the block's amax in amax_out). The quotient takes the three-operation
 // form unless some lane of the wave has a scale below kFastScaleMin (the
 // ballot keeps the choice wave-uniform); lanes outside any block must have
 // left the wave before the call.
-__device__ __forceinline__ float quant_block_bf16(const uint4 v0, const uint4 v1, uint2& o0, uint2& o1) {
+__device__ __forceinline__ float quant_block_bf16(const uint4 v0, const uint4 v1, uint2& o0, uint2& o1,
+                                                  float& amax_out) {
   float m = 0.0f;
   m = absmax2(v0.x, m); m = absmax2(v0.y, m); m = absmax2(v0.z, m); m = absmax2(v0.w, m);
   m = absmax2(v1.x, m); m = absmax2(v1.y, m); m = absmax2(v1.z, m); m = absmax2(v1.w, m);
@@ -129,7 +130,12 @@ __device__ __forceinline__ float quant_block_bf16(const uint4 v0, const uint4 v1
     o0 = make_uint2(0u, 0u);
     o1 = make_uint2(0u, 0u);
   }
+  amax_out = amax;
   return s;
+}
+__device__ __forceinline__ float quant_block_bf16(const uint4 v0, const uint4 v1, uint2& o0, uint2& o1) {
+  float amax;
+  return quant_block_bf16(v0, v1, o0, o1, amax);
 }
 
 }  // namespace fp8bs

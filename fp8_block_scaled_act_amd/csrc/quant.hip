@@ -344,6 +344,39 @@ __global__ __launch_bounds__(kThreads) void tensor_apply_kernel(
   if (head) scale[0] = s;
 }
 
+// ---------------------------------------------------------------------------
+// Block and per-tensor quantization of the same X (both quantize the
+// activation of the large-M workload): the block kernel above, with
+// 1024-thread workgroups that also write the max of their 128 block maxima,
+// is the per-tensor amax's first pass, so X is read twice rather than three
+// times; the second pass is tensor_apply_kernel over those partials.
+// ---------------------------------------------------------------------------
+constexpr int kBTThreads = 1024;
+
+__global__ __launch_bounds__(kBTThreads) void act_quant_block_partial_kernel(
+    const uint4* __restrict__ x, uint2* __restrict__ q, float* __restrict__ scale,
+    float* __restrict__ partial, int64_t nblocks) {
+  __shared__ float lds[kBTThreads / 64];
+  const int64_t blk = (static_cast<int64_t>(blockIdx.x) * kBTThreads + threadIdx.x) >> 3;
+  const int sub = threadIdx.x & 7;
+  float amax = 0.0f;
+  if (blk < nblocks) {   // whole 8-lane groups
+    const uint4 v0 = x[blk * 16 + sub];
+    const uint4 v1 = x[blk * 16 + 8 + sub];
+    uint2 o0, o1;
+    const float s = quant_block_bf16(v0, v1, o0, o1, amax);
+    q[blk * 16 + sub] = o0;
+    q[blk * 16 + 8 + sub] = o1;
+    if (sub == 0) scale[blk] = s;
+  }
+  amax = block_max<kBTThreads>(amax, lds);
+  if (threadIdx.x == 0) partial[blockIdx.x] = amax;
+}
+
+int64_t block_tensor_partials(int64_t M, int64_t K) {
+  return (M * (K / 128) * 8 + kBTThreads - 1) / kBTThreads;
+}
+
 int tensor_grid(int64_t numel, int num_cus) {
   const int64_t nvec = (numel >> 3) + 1;
   const int64_t per_wg = static_cast<int64_t>(kThreads) * kVecPerThread;
@@ -506,6 +539,43 @@ int fp8_amax_quant_tensor(const void* x_bf16, int64_t numel, void* q_e4m3, float
   ga = std::min<int64_t>(ga, 8LL * dev.num_cus);
   hipLaunchKernelGGL(tensor_apply_kernel, dim3(static_cast<unsigned>(ga)), dim3(kThreads), 0, st, x,
                      q, scale, partial, g, numel);
+  return launch_status();
+}
+
+size_t fp8_act_quant_block_tensor_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 1 || K < 128 || K % 128 != 0 || M > (INT64_MAX / K)) return 0;
+  return static_cast<size_t>((block_tensor_partials(M, K) * 4 + 255) / 256 * 256);
+}
+
+int fp8_act_quant_block_tensor(const void* x_bf16, int64_t M, int64_t K, void* qb_e4m3, float* block_scale,
+                               void* qt_e4m3, float* tensor_scale, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (!x_bf16 || !qb_e4m3 || !block_scale || !qt_e4m3 || !tensor_scale) return FP8BS_ERR_NULL;
+  if (M < 1 || K < 128 || K % 128 != 0 || M > (INT64_MAX / K)) return FP8BS_ERR_SHAPE;
+  if (!aligned(x_bf16, 16) || !aligned(qb_e4m3, 16) || !aligned(block_scale, 4) || !aligned(qt_e4m3, 16) ||
+      !aligned(tensor_scale, 4))
+    return FP8BS_ERR_ALIGN;
+  const int64_t np = block_tensor_partials(M, K);
+  if (np > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  const size_t need = fp8_act_quant_block_tensor_workspace_bytes(M, K);
+  if (!workspace || workspace_bytes < need) return FP8BS_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return FP8BS_ERR_ALIGN;
+  const DeviceInfo dev = current_device();
+  if (dev.status != FP8BS_OK) return dev.status;
+  hipStream_t st = as_stream(stream);
+  float* partial = static_cast<float*>(workspace);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(act_quant_block_partial_kernel, dim3(static_cast<unsigned>(np)), dim3(kBTThreads), 0, st,
+                     static_cast<const uint4*>(x_bf16), static_cast<uint2*>(qb_e4m3), block_scale, partial,
+                     M * (K / 128));
+  if (hipGetLastError() != hipSuccess) return FP8BS_ERR_LAUNCH;
+  const int64_t numel = M * K;
+  const int64_t nvec = (numel >> 3) + 1;
+  int64_t ga = (nvec + kThreads * 2 - 1) / (kThreads * 2);
+  ga = std::min<int64_t>(ga, 8LL * dev.num_cus);
+  hipLaunchKernelGGL(tensor_apply_kernel, dim3(static_cast<unsigned>(ga)), dim3(kThreads), 0, st,
+                     static_cast<const uint16_t*>(x_bf16), static_cast<uint8_t*>(qt_e4m3), tensor_scale, partial,
+                     static_cast<int>(np), numel);
   return launch_status();
 }
 

@@ -198,6 +198,30 @@ int fp8_gemm_tensorscaled(const void* a_e4m3, const float* a_scale,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Block AND per-tensor quantization of the same bf16 x [M, K] (the large-M
+ * workload quantizes its activation both ways): exactly the outputs of
+ * fp8_act_quant_block(x) -> (qb_e4m3, block_scale) and
+ * fp8_amax_quant_tensor(x) -> (qt_e4m3, tensor_scale), bit for bit. The block
+ * kernel also writes one partial maximum per workgroup (the maximum of its
+ * blocks' exact amax), which is the per-tensor amax's first pass
+ * (TensorRT-LLM PR "Size the per-tensor FP8 dynamic-quant amax grid to the
+ * input", section "Description": a grid sized to the input, no single-address
+ * atomic), so x is read twice instead of three times.
+ *
+ *   qb_e4m3 [M, K], block_scale [M, K/128] fp32; qt_e4m3 [M, K], tensor_scale
+ *   [1] fp32 (written on the device); alignments as the two calls above
+ *   workspace  at least fp8_act_quant_block_tensor_workspace_bytes(M, K)
+ *              bytes (4 per 128 blocks of x), 16-byte aligned; contents on
+ *              entry do not matter; not shared by concurrent calls
+ * Requires M >= 1, K >= 128, K % 128 == 0. Errors as above.
+ */
+size_t fp8_act_quant_block_tensor_workspace_bytes(int64_t M, int64_t K);
+int fp8_act_quant_block_tensor(const void* x_bf16, int64_t M, int64_t K,
+                               void* qb_e4m3, float* block_scale,
+                               void* qt_e4m3, float* tensor_scale,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Block act-quant and block-scaled GEMM in one call, for decode batches:
  *     (A_q, a_scale) = the 1x128 block quantization of x (fp8_act_quant_block)
  *     C = fp8_gemm_blockscaled(A_q, a_scale, w_e4m3, w_scale)

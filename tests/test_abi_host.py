@@ -163,3 +163,18 @@ def test_act_quant_gemm_argument_errors(L):
     assert ws(4096, 4096, 7168) == 4096 * 7168 + 4096 * 56 * 4
     assert f(P, P, P, P, 17, 128, 128, None, 0, None) == EWS
     assert f(P, P, P, P, 17, 128, 128, P, ws(17, 128, 128) - 1, None) == EWS
+
+
+def test_act_quant_block_tensor_argument_errors(L):
+    f = L.fp8_act_quant_block_tensor
+    ws = L.fp8_act_quant_block_tensor_workspace_bytes
+    assert ws(16384, 2048) == 16384 * 16 * 8 // 1024 * 4
+    assert ws(1, 128) == 256 and ws(0, 128) == 0 and ws(4, 100) == 0
+    assert f(None, 4, 128, P, P, P, P, P, 256, None) == ENULL
+    assert f(P, 4, 128, P, P, None, P, P, 256, None) == ENULL
+    assert f(P, 4, 100, P, P, P, P, P, 256, None) == ESHAPE
+    assert f(P, 0, 128, P, P, P, P, P, 256, None) == ESHAPE
+    assert f(PU, 4, 128, P, P, P, P, P, 256, None) == EALIGN
+    assert f(P, 4, 128, P, P, PU, P, P, 256, None) == EALIGN
+    assert f(P, 4, 128, P, P, P, P, None, 0, None) == EWS
+    assert f(P, 4, 128, P, P, P, P, P, 255, None) == EWS
