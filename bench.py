@@ -40,8 +40,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="c5", choices=["c5", "c4", "c3", "c2", "c1", "aq32", "copy"],
                    help="copy: a plain 256 MiB device-to-device copy (HBM reference for counters); "
                         "aq32: block act-quant of the prefill activation given as float32")
@@ -263,7 +263,9 @@ def time_steps(torch, wl, steps, warmup, graph):
     """Warm up, then time exactly `steps` steps between two HIP events on the
     launch stream (torch's current stream, where the library enqueues). Then,
     for the per-stage figures, time `steps` back-to-back launches of each
-    stage alone the same way (average duration per launch)."""
+    stage alone the same way (average duration per launch), after a pass that
+    gives the spread: each launch between its own pair of events, or, with
+    graphs, ten replays of the stage's graph."""
     st = torch.cuda.current_stream()
     for i in range(warmup):
         for _, fn, _, _ in wl.stages:
@@ -316,6 +318,26 @@ def time_steps(torch, wl, steps, warmup, graph):
             torch.cuda.synchronize()
             gs.replay()
             torch.cuda.synchronize()
+        # spread (median, p10, p90 of per-launch times)
+        if gs is not None:
+            reps = []
+            for _ in range(10):
+                a, b = ev(), ev()
+                a.record(st)
+                gs.replay()
+                b.record(st)
+                torch.cuda.synchronize()
+                reps.append(a.elapsed_time(b) / steps)
+        else:
+            evs = [ev() for _ in range(steps + 1)]
+            evs[0].record(st)
+            for i in range(steps):
+                fn(i)
+                evs[i + 1].record(st)
+            torch.cuda.synchronize()
+            reps = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+        spread = (float(np.median(reps)), float(np.percentile(reps, 10)), float(np.percentile(reps, 90)))
+        # the average: back-to-back launches between one pair of events
         a, b = ev(), ev()
         a.record(st)
         if gs is not None:
@@ -325,7 +347,7 @@ def time_steps(torch, wl, steps, warmup, graph):
                 fn(i)
         b.record(st)
         torch.cuda.synchronize()
-        per_stage.append(a.elapsed_time(b) / steps)
+        per_stage.append((a.elapsed_time(b) / steps, spread))
     return step_ms, per_stage, wall
 
 
@@ -396,8 +418,10 @@ def main():
     for j, (name, _, nbytes, flops) in enumerate(wl.stages):
         e = {"algorithmic_bytes": nbytes}
         if per_stage is not None:
-            us = float(per_stage[j]) * 1e3
+            avg_ms, (med, p10, p90) = per_stage[j]
+            us = float(avg_ms) * 1e3
             e["us_per_launch"] = us
+            e["us_median"], e["us_p10"], e["us_p90"] = med * 1e3, p10 * 1e3, p90 * 1e3
             e["GB/s"] = nbytes / (us * 1e-6) / 1e9
             e["hbm_frac"] = e["GB/s"] / HBM_PEAK_GBS
             if flops:
@@ -460,7 +484,9 @@ def main():
         "config": wl.config,
         "timing": ("step: HIP events around all steps" + (" (HIP graph replay)" if args.graph else "")
                    + "; stages: HIP events around back-to-back launches of each stage"
-                   + (" (each stage replayed from a graph of its own)" if args.graph else "")),
+                   + (" (each stage replayed from a graph of its own)" if args.graph else "")
+                   + "; us_median/p10/p90: " + ("over ten replays of the stage's graph" if args.graph
+                                               else "each launch between its own pair of events")),
         "stages": stages,
         "roofline": roofline,
         "cpu_baseline": cpu,
