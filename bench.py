@@ -46,7 +46,10 @@ def parse():
                    help="copy: a plain 256 MiB device-to-device copy (HBM reference for counters); "
                         "aq32: block act-quant of the prefill activation given as float32")
     p.add_argument("--M", type=int, default=None, help="rows for c2/c3")
-    p.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
+    p.add_argument("--graph", dest="graph", action="store_true", default=True,
+                   help="replay the steps from a HIP graph (the default)")
+    p.add_argument("--no-graph", dest="graph", action="store_false",
+                   help="launch every step from the host instead of replaying a graph")
     p.add_argument("--rotate", type=int, default=0,
                    help="input copies rotated across steps (0: enough copies for >= 512 MiB of distinct "
                         "inputs, twice the last-level cache, capped at 64)")
