@@ -1002,10 +1002,13 @@ struct DecodePlan {
 
 // K split for the decode kernel: enough workgroups to keep ~512 in flight,
 // at most kDecMaxKb K blocks per split
+// (a W of at most kDecSmallW bytes is not worth spreading: one split unless K
+// needs more, so no workspace and no second kernel)
+constexpr int64_t kDecSmallW = int64_t{1} << 21;
 inline DecodePlan decode_plan(int64_t N, int64_t K) {
   const int64_t KB = K / kBK;
   const int64_t ntiles = (N + kDecRows - 1) / kDecRows;
-  int64_t want = (512 + ntiles - 1) / ntiles;
+  int64_t want = N * K <= kDecSmallW ? 1 : (512 + ntiles - 1) / ntiles;
   want = std::max<int64_t>(want, (KB + kDecMaxKb - 1) / kDecMaxKb);
   want = std::min<int64_t>(want, KB);
   int kb_per = static_cast<int>((KB + want - 1) / want);
