@@ -542,12 +542,13 @@ void gemm_blockscaled_tiled_kernel(
 // Small M (M <= 16): workgroup = 16 W rows (one MFMA tile of n) over the
 // whole of K, sixteen waves; wave w takes K blocks w, w+16, w+32, ... and
 // keeps kDecDepth of them in flight, W fragments and A fragments loaded
-// straight from global memory
-// into registers (A is small and stays in L2). Each K block is one MFMA per
-// 16 activation rows plus the scale FMAs. The sixteen partial sums are added
-// through LDS in wave order, so the result is deterministic and no second
-// kernel or workspace is needed. Every workgroup reads all of A (through
-// L2), which costs little while A is at most 16 rows.
+// straight from global memory into registers (A is small and stays in L2).
+// Each K block is one MFMA per 16 activation rows plus the scale FMAs. The
+// sixteen partial sums are added through LDS in wave order, so the result is
+// deterministic and no second kernel or workspace is needed. Every workgroup
+// reads all of A (through L2), which costs little while A is at most 16 rows.
+// (For M <= 2, and for K too large for A to fit in LDS otherwise, the
+// LDS-staged kernel below serves instead.)
 // ---------------------------------------------------------------------------
 #ifndef FP8BS_DEC_WAVES
 #define FP8BS_DEC_WAVES 16

@@ -120,8 +120,9 @@ int fp8_amax_quant_tensor(const void* x_bf16, int64_t numel,
  *   c_bf16   [M, N] bf16, 16-byte aligned           (output, RNE from fp32)
  *   workspace  at least fp8_gemm_blockscaled_workspace_bytes(M, N, K) bytes,
  *              16-byte aligned (NULL allowed when that size is 0, which is
- *              the case unless 16 < M <= 64); contents on entry do not
- *              matter; not to be shared by calls that can run concurrently
+ *              the case unless 16 < M <= 64 and N*K > 2^21); contents on
+ *              entry do not matter; not to be shared by calls that can run
+ *              concurrently
  * Requires M >= 1, N >= 128, K >= 128, N % 128 == 0, K % 128 == 0,
  * K <= 4194304 (32-bit offsets within a 256-row tile), and K <= 65536 when
  * 16 < M <= 64 (that path splits K into at most 32 parts).
