@@ -547,8 +547,8 @@ void gemm_blockscaled_tiled_kernel(
 // sixteen partial sums are added through LDS in wave order, so the result is
 // deterministic and no second kernel or workspace is needed. Every workgroup
 // reads all of A (through L2), which costs little while A is at most 16 rows.
-// (For M <= 2, and for K too large for A to fit in LDS otherwise, the
-// LDS-staged kernel below serves instead.)
+// (For M <= 2, while A fits in LDS, the LDS-staged kernel below serves
+// instead.)
 // ---------------------------------------------------------------------------
 #ifndef FP8BS_DEC_WAVES
 #define FP8BS_DEC_WAVES 16
