@@ -99,7 +99,7 @@ def test_c5_large_m_sampled_rows():
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (17, 256, 384), (129, 384, 256),
                                    (200, 128, 1024), (255, 512, 128), (300, 640, 640),
-                                   (300, 384, 2432), (133, 256, 1152)])
+                                   (300, 384, 2432), (133, 256, 1152), (65, 256, 640)])
 def test_ragged_shapes(M, N, K):
     rng = np.random.default_rng(M + N + K)
     a = synth.f64_to_bf16_bits(rng.standard_t(3.0, size=(M, K)))
