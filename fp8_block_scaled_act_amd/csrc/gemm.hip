@@ -22,6 +22,11 @@
 #include "device_common.h"
 #include "host_common.h"
 
+// Build-time knobs kept for measurement (the defaults are the measured best):
+// FP8BS_DMA_ROWS, the MFMA rows of a block over which the next block's copies
+// are spread; FP8BS_DEC_WAVES, the waves of a small-M decode workgroup;
+// FP8BS_GEMM_TILE, 0 to pick the tile shape by problem size, else one shape
+// for every size (1: 128x128, 2: 256x256, 3: 256x128 with three stages).
 #ifndef FP8BS_DMA_ROWS
 #define FP8BS_DMA_ROWS 4
 #endif
