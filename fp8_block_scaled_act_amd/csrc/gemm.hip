@@ -267,9 +267,10 @@ void gemm_blockscaled_tiled_kernel(
 
   const uint32_t lds0 = lds_addr(lds);
   // Copy p of this wave's part of block kb (p < kPer: W copies, then A
-  // copies; the scale copy goes with p == 0). Inside the K loop the copies
-  // of the block being prefetched are spread over the first MFMA rows.
-  // Each buffer starts at column 128*kb of the tile's first row.
+  // copies; the copies of a scale chunk go with p == 0 of the chunk's first
+  // block). Inside the K loop the copies of the block being prefetched are
+  // spread over the first MFMA rows. Each buffer starts at column 128*kb of
+  // the tile's first row.
   auto issue_part = [&](int kb, int p) {
     const uint32_t st = lds0 + (kb % STAGES) * T::kStageBytes;
     const uint32_t cb = static_cast<uint32_t>(kb) * kBK;
