@@ -235,8 +235,11 @@ __device__ __forceinline__ void store_nt(uint2 v, uint2* p) {
   __builtin_nontemporal_store(w, reinterpret_cast<u32x2_nt*>(p));
 }
 
-// the same with kVecPerThread vectors per thread in flight and the codes
-// stored non-temporally
+// the same with kVecPerThread vectors per thread in flight, the codes
+// stored non-temporally, and the tensor walked from its end: the first pass
+// walked it from the start, so the last-level cache holds its most recently
+// read part, which this pass then reads first (when the input is larger
+// than that cache, a walk in the same order would find every line evicted)
 template <bool kFast>
 __device__ __forceinline__ void quant_range_nt(const uint4* xv, uint2* qv, int64_t nvec,
                                                 int64_t first, int64_t stride, float s, float r,
@@ -245,18 +248,18 @@ __device__ __forceinline__ void quant_range_nt(const uint4* xv, uint2* qv, int64
   for (; i + (kVecPerThread - 1) * stride < nvec; i += kVecPerThread * stride) {
     uint4 v[kVecPerThread];
 #pragma unroll
-    for (int j = 0; j < kVecPerThread; ++j) v[j] = xv[i + j * stride];
+    for (int j = 0; j < kVecPerThread; ++j) v[j] = xv[nvec - 1 - (i + j * stride)];
 #pragma unroll
     for (int j = 0; j < kVecPerThread; ++j) {
       uint2 o = quant8<kFast>(v[j], s, r);
       if (zero) o = make_uint2(0u, 0u);
-      store_nt(o, qv + i + j * stride);
+      store_nt(o, qv + nvec - 1 - (i + j * stride));
     }
   }
   for (; i < nvec; i += stride) {
-    uint2 o = quant8<kFast>(xv[i], s, r);
+    uint2 o = quant8<kFast>(xv[nvec - 1 - i], s, r);
     if (zero) o = make_uint2(0u, 0u);
-    store_nt(o, qv + i);
+    store_nt(o, qv + nvec - 1 - i);
   }
 }
 
