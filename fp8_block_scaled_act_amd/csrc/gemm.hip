@@ -545,64 +545,144 @@ void gemm_blockscaled_tiled_kernel(
 // ---------------------------------------------------------------------------
 // Decode kernels. At decode shapes the GEMM is bound by streaming W from HBM.
 //
-// Small M (M <= 16): workgroup = 16 W rows (one MFMA tile of n) over the
-// whole of K, sixteen waves; wave w takes K blocks w, w+16, w+32, ... and
-// keeps kDecDepth of them in flight, W fragments and A fragments loaded
-// straight from global memory into registers (A is small and stays in L2).
-// Each K block is one MFMA per 16 activation rows plus the scale FMAs. The
-// sixteen partial sums are added through LDS in wave order, so the result is
-// deterministic and no second kernel or workspace is needed. Every workgroup
-// reads all of A (through L2), which costs little while A is at most 16 rows.
-// (For M <= 2, while A fits in LDS, the LDS-staged kernel below serves
-// instead.)
+// Small M (M <= 16): a workgroup takes R W rows over the whole of K, sixteen
+// waves; the waves split K into steps of P K blocks (P = 16 / R), wave w
+// taking steps w, w+16, w+32, ... and keeping kDecDepth of them in flight,
+// W fragments and A fragments loaded straight from global memory into
+// registers (A is small and stays in L2). Each step is one MFMA plus the
+// scale FMAs. The sixteen waves' partial sums are added through LDS in a
+// fixed order, so the result is deterministic and no second kernel or
+// workspace is needed. Every workgroup reads all of A (through L2), which
+// costs little while A is at most 16 rows. (Staging A in LDS before the K
+// loop, as the fused kernel below does with the quantized X, measured
+// slower for every M: 5.8 against 5.4 us at M = 1 with packed blocks.)
+//
+// Packed K blocks (P > 1, for M <= R): a 16x16 MFMA tile has 16 W rows, but
+// with R = 16 / P W rows per workgroup the grid has P times as many
+// workgroups, so that every CU streams W (N = 2048: 128 workgroups of 16
+// rows leave half of the 256 CUs idle; 256 workgroups of 8 rows read the
+// 14.7 MB of W in 4.2 instead of 5.1 us in a read-only probe). The MFMA's
+// 16 rows (and 16 activation columns) are then P groups of R: group g
+// carries K block P*s + g of the same R W rows and of activation rows
+// 0..R-1, and the diagonal blocks of its 16x16 result (W group g against
+// activation group g) are the partial sums of those blocks; the
+// off-diagonal blocks are discarded. Lane l supplies row (l%16)%R of group
+// (l%16)/R; its four outputs lie in one group, and they are kept when that
+// group is its own column's.
 // ---------------------------------------------------------------------------
 #ifndef FP8BS_DEC_WAVES
 #define FP8BS_DEC_WAVES 16
 #endif
 constexpr int kDecWaves = FP8BS_DEC_WAVES;
 constexpr int kDecStreamMaxM = 16;
+// K blocks packed into one MFMA for a small-M decode GEMM (rows per
+// workgroup 16 / P must hold the M activation rows)
+constexpr int kDecPackMaxM = 8;
+inline int decode_pack(int64_t M) { return M <= kDecPackMaxM ? 2 : 1; }
 
-// MT: 16-row groups of A (M <= 16*MT); kDecDepth: K blocks in flight per wave;
-// TS: one scale per tensor (sa[0] * sw[0] for every block)
-template <int MT, int kDecDepth, bool TS>
+// Sum over each row of 16 lanes by DPP lane swaps: pairs i^1 and i^2 (quad
+// permutations), then the mirror images within 8 and within 16 lanes. Each
+// step adds a lane's value to its partner's, so every lane of a row ends
+// with the same bits. All lanes of the wave must be active.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp_f32<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp_f32<0x141>(v);   // row_half_mirror
+  v += dpp_f32<0x140>(v);   // row_mirror
+  return v;
+}
+
+// Final sums and bf16 stores of a small-M decode workgroup, called by every
+// thread after a barrier. red holds the waves' float4 results, lane l of
+// wave w at red[w * 64 + l]; lane l holds D[n = 4*(l/16) + r][m = l%16] of
+// its wave's MFMA tile. Output group o = (quad q = o / M, activation row
+// m = o % M) is W rows n0 + 4q .. +3 against activation row m; in K-block
+// group g it sits in lane 16q + m + 5*g*R (W rows and activation columns
+// both shifted by g*R). A row of 16 threads takes one output group: thread
+// i adds the P group terms of wave i in group order, then the row adds the
+// waves by lane swaps. The order is fixed, so the result is deterministic.
+template <int P>
+__device__ __forceinline__ void decode_store(const float4* red, int M, int64_t n0, int64_t N, uint16_t* C) {
+  constexpr int R = 16 / P;
+  static_assert(kDecWaves <= 16, "one wave per thread of a 16-thread row");
+  const int nout = (R / 4) * M;
+  const int i = threadIdx.x & 15;
+  for (int ob = 0; ob < nout; ob += 4 * kDecWaves) {
+    const int o = ob + static_cast<int>(threadIdx.x >> 4);
+    const int q = o / M, m = o - q * M;
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (o < nout && i < kDecWaves) {
+      const int l0 = 16 * q + m;
+      v = red[i * 64 + l0];
+#pragma unroll
+      for (int g = 1; g < P; ++g) {
+        const float4 u = red[i * 64 + l0 + 5 * g * R];
+        v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+      }
+    }
+    v.x = row16_sum(v.x);
+    v.y = row16_sum(v.y);
+    v.z = row16_sum(v.z);
+    v.w = row16_sum(v.w);
+    if (o < nout && i == 0) {
+      uint2 out;
+      out.x = bf16x2_rne(v.x, v.y);
+      out.y = bf16x2_rne(v.z, v.w);
+      *reinterpret_cast<uint2*>(C + m * N + n0 + 4 * q) = out;
+    }
+  }
+}
+
+// P: K blocks packed per MFMA (M <= 16 / P); kDecDepth: steps in flight per
+// wave; TS: one scale per tensor (sa[0] * sw[0] for every block)
+template <int P, int kDecDepth, bool TS>
 __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(kDecWaves / 4, kDecWaves / 4)))
 void gemm_blockscaled_decode_stream_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, uint16_t* __restrict__ C, int M, int64_t N, int64_t K) {
-  __shared__ float4 red[kDecWaves][MT][64];
+  constexpr int R = 16 / P;
+  __shared__ float4 red[kDecWaves * 64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * R;
   const int KB = static_cast<int>(K / kBK);
 
-  // lane l supplies W row n0 + l%16 and A rows 16j + l%16 (rows past M read
-  // row M-1: valid memory, results never stored), K bytes 32*(l/16) ..+32
+  // lane l supplies W row n0 + rsub and A row rsub (rows past M read row
+  // M-1: valid memory, results never stored) of K block P*s + grp of step s,
+  // bytes 32*(l/16) ..+32 of the block
+  const int rsub = (lane & 15) % R;
+  const int grp = (lane & 15) / R;
   const int koff = 32 * (lane >> 4);
-  const uint8_t* wp = W + (n0 + (lane & 15)) * K + koff;
-  const uint8_t* ap[MT];
-  const float* sp[MT];
-#pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    const int64_t m = min(j * 16 + (lane & 15), M - 1);
-    ap[j] = A + m * K + koff;
-    sp[j] = sa + m * KB;
-  }
+  const uint8_t* wp = W + (n0 + rsub) * K + koff;
+  const int64_t am = min(rsub, M - 1);
+  const uint8_t* ap = A + am * K + koff;
+  const float* sp = sa + am * KB;
   const float* swrow = sw + (n0 / 128) * KB;
 
-  // this wave's K blocks: kb = wave + kDecWaves * t, t = 0 .. nt-1
-  const int nt = KB > wave ? (KB - wave + kDecWaves - 1) / kDecWaves : 0;
+  // this wave's steps: s = wave + kDecWaves * t, t = 0 .. nt-1; a lane
+  // whose block is past K (last step, KB not a multiple of P) loads
+  // nothing and contributes zeros
+  const int S = (KB + P - 1) / P;
+  const int nt = S > wave ? (S - wave + kDecWaves - 1) / kDecWaves : 0;
   uint4 wq[kDecDepth][2];
-  uint4 aq[kDecDepth][MT][2];
-  float sq[kDecDepth][MT];
+  uint4 aq[kDecDepth][2];
+  float sq[kDecDepth];
   auto load = [&](int d, int t) {
-    const int64_t kb = wave + static_cast<int64_t>(kDecWaves) * t;
-    wq[d][0] = *reinterpret_cast<const uint4*>(wp + kb * kBK);
-    wq[d][1] = *reinterpret_cast<const uint4*>(wp + kb * kBK + 16);
-#pragma unroll
-    for (int j = 0; j < MT; ++j) {
-      aq[d][j][0] = *reinterpret_cast<const uint4*>(ap[j] + kb * kBK);
-      aq[d][j][1] = *reinterpret_cast<const uint4*>(ap[j] + kb * kBK + 16);
-      if constexpr (!TS) sq[d][j] = sp[j][kb];
+    const int64_t kb = static_cast<int64_t>(wave + kDecWaves * t) * P + grp;
+    if (P == 1 || kb < KB) {
+      wq[d][0] = *reinterpret_cast<const uint4*>(wp + kb * kBK);
+      wq[d][1] = *reinterpret_cast<const uint4*>(wp + kb * kBK + 16);
+      aq[d][0] = *reinterpret_cast<const uint4*>(ap + kb * kBK);
+      aq[d][1] = *reinterpret_cast<const uint4*>(ap + kb * kBK + 16);
+      if constexpr (!TS) sq[d] = sp[kb];
+    } else {
+      wq[d][0] = wq[d][1] = make_uint4(0, 0, 0, 0);
+      aq[d][0] = aq[d][1] = make_uint4(0, 0, 0, 0);
+      if constexpr (!TS) sq[d] = 0.0f;
     }
   };
   const float cst = TS ? sa[0] * sw[0] : 0.0f;
@@ -610,9 +690,7 @@ void gemm_blockscaled_decode_stream_kernel(
   for (int d = 0; d < kDecDepth; ++d)
     if (d < nt) load(d, d);
 
-  v4f acc[MT];
-#pragma unroll
-  for (int j = 0; j < MT; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   for (int t0 = 0; t0 < nt; t0 += kDecDepth) {
 #pragma unroll
     for (int d = 0; d < kDecDepth; ++d) {
@@ -620,80 +698,53 @@ void gemm_blockscaled_decode_stream_kernel(
       if (t < nt) {
         const v8i wf = v8i{(int)wq[d][0].x, (int)wq[d][0].y, (int)wq[d][0].z, (int)wq[d][0].w,
                            (int)wq[d][1].x, (int)wq[d][1].y, (int)wq[d][1].z, (int)wq[d][1].w};
-        v8i af[MT];
-        float cs[MT];
-        const float swb = TS ? 1.0f : swrow[wave + kDecWaves * t];
-#pragma unroll
-        for (int j = 0; j < MT; ++j) {
-          af[j] = v8i{(int)aq[d][j][0].x, (int)aq[d][j][0].y, (int)aq[d][j][0].z, (int)aq[d][j][0].w,
-                      (int)aq[d][j][1].x, (int)aq[d][j][1].y, (int)aq[d][j][1].z, (int)aq[d][j][1].w};
-          cs[j] = TS ? cst : sq[d][j] * swb;
-        }
+        const v8i af = v8i{(int)aq[d][0].x, (int)aq[d][0].y, (int)aq[d][0].z, (int)aq[d][0].w,
+                           (int)aq[d][1].x, (int)aq[d][1].y, (int)aq[d][1].z, (int)aq[d][1].w};
+        const int kb = (wave + kDecWaves * t) * P + grp;
+        const float swb = TS ? 1.0f : (P == 1 || kb < KB ? swrow[kb] : 0.0f);
+        const float cs = TS ? cst : sq[d] * swb;
         if (t + kDecDepth < nt) load(d, t + kDecDepth);
+        const v4f p = mfma_16x16x128_fp8(wf, af);
 #pragma unroll
-        for (int j = 0; j < MT; ++j) {
-          const v4f p = mfma_16x16x128_fp8(wf, af[j]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(p[r], cs[j], acc[j][r]);
-        }
+        for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(p[r], cs, acc[r]);
       }
     }
   }
 
-  // lane holds D[n = n0 + 4*(lane/16) + r][m = 16j + lane%16]; add the
-  // waves' partial sums in wave order
-#pragma unroll
-  for (int j = 0; j < MT; ++j) red[wave][j][lane] = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+  red[wave * 64 + lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
   __syncthreads();
-  const int t = threadIdx.x;
-  if (t < MT * 64) {
-    const int j = t / 64, l = t % 64;
-    const int m = j * 16 + (l & 15);
-    if (m < M) {
-      float4 s = red[0][j][l];
-#pragma unroll
-      for (int w = 1; w < kDecWaves; ++w) {
-        const float4 v = red[w][j][l];
-        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-      }
-      const int64_t n = n0 + 4 * (l >> 4);
-      uint2 o;
-      o.x = bf16x2_rne(s.x, s.y);
-      o.y = bf16x2_rne(s.z, s.w);
-      *reinterpret_cast<uint2*>(C + m * N + n) = o;
-    }
-  }
+  decode_store<P>(red, M, n0, N, C);
 }
 
 template <bool TS>
 int launch_decode_stream(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c,
                          int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_blockscaled_decode_stream_kernel<1, 4, TS>), dim3(static_cast<unsigned>(N / 16)),
-                     dim3(64 * kDecWaves), 0, st, a, sa, w, sw, c, static_cast<int>(M), N, K);
+  if (decode_pack(M) == 2)
+    hipLaunchKernelGGL((gemm_blockscaled_decode_stream_kernel<2, 4, TS>), dim3(static_cast<unsigned>(N / 8)),
+                       dim3(64 * kDecWaves), 0, st, a, sa, w, sw, c, static_cast<int>(M), N, K);
+  else
+    hipLaunchKernelGGL((gemm_blockscaled_decode_stream_kernel<1, 4, TS>), dim3(static_cast<unsigned>(N / 16)),
+                       dim3(64 * kDecWaves), 0, st, a, sa, w, sw, c, static_cast<int>(M), N, K);
   return FP8BS_OK;
 }
 
 // ---------------------------------------------------------------------------
-// Small-M decode GEMM with the activations in LDS (M <= kDecLdsMaxM), and
-// the same kernel with the block act-quant fused in (M <= kFusedMaxM).
+// Small-M decode GEMM with the block act-quant fused in (M <= kFusedMaxM):
+// C = A_q . W^T with (A_q, sa) the 1x128 block quantization of the bf16
+// activations X, in one launch; the quantized activations never go to
+// global memory.
 //
-// Same workgroup shape and K order as the streaming kernel above: 16 W rows
-// per workgroup over the whole of K, wave w taking K blocks w, w+16, ...
-// Each workgroup first issues its waves' first W loads, then stages all of A
-// (M x K codes and the M x K/128 scales) in LDS while those loads are in
-// flight, and runs the K loop with A fragments and scales read from LDS: the
-// A loads of the streaming kernel go through L1 and L2 once per K block and
-// wave and their latency adds to every block's (measured at N = 2048,
-// K = 7168: 10.6 us at M = 16 with them, 6.0 us with A not loaded at all).
-//
-// QUANT: C = A_q . W^T with (A_q, sa) the 1x128 block quantization of the
-// bf16 activations X, in one launch (the quantized activations never go to
-// global memory): the staging step quantizes X with the act-quant kernel's
-// rule and lane mapping (eight lanes per 1x128 block, the same helper).
-// The arithmetic after staging is the streaming kernel's, operation for
-// operation, so the results are those of the two-launch path bit for bit.
-// Every workgroup quantizes all of X: that redundant work grows with M, so
-// the fused form serves the smallest M only (kFusedMaxM).
+// Same workgroup shape, K order and packing as the streaming kernel above:
+// R W rows per workgroup over the whole of K, wave w taking steps w, w+16,
+// ... of P K blocks each. Each workgroup first issues its waves' first W
+// loads, then quantizes all of X into LDS (codes and scales) while those
+// loads are in flight, with the act-quant kernel's rule and lane mapping
+// (eight lanes per 1x128 block, the same helper), and runs the K loop with
+// A fragments and scales read from LDS. The arithmetic after that is the
+// streaming kernel's, operation for operation, so the results are those of
+// the two-launch path (act-quant, then the GEMM) bit for bit. Every
+// workgroup quantizes all of X: that redundant work grows with M, so the
+// fused form serves the smallest M only.
 //
 // LDS: the wave partial sums (16 KiB), the scales [M][K/128], then the codes
 // of K block kb at kb*128*M: half h (16 bytes) of quarter q (32 bytes) of
@@ -703,30 +754,21 @@ int launch_decode_stream(const uint8_t* a, const float* sa, const uint8_t* w, co
 constexpr int kFusedLdsBytes = 160 * 1024;
 constexpr int kFusedRedBytes = kDecWaves * 64 * 16;
 // largest M for the one-kernel act-quant + GEMM: above it the two launches
-// are faster (measured at N = 2048, K = 7168: one kernel 6.5 / 8.6 / 10.5 us
-// at M = 1 / 4 / 8 against 9.4 / 10.4 / 11.3 us, but 12.7 against 12.2 us
-// at M = 12)
-constexpr int64_t kFusedMaxM = 8;
+// are faster
+constexpr int64_t kFusedMaxM = 4;
 
 __host__ __device__ inline int64_t fused_scale_bytes(int64_t M, int64_t K) { return (M * (K / kBK) * 4 + 15) / 16 * 16; }
-// largest M for which the GEMM alone stages A in LDS: the staging step runs
-// before the K loop and grows with M, the per-block A loads it saves cost
-// less from M = 4 on (N = 2048, K = 7168: 6.2 against 6.9 us at M = 1, 7.9
-// against 7.8 us at M = 4, 12.8 against 10.6 us at M = 16)
-constexpr int64_t kDecLdsMaxM = 2;
-inline bool lds_fits(int64_t M, int64_t K) {
-  return kFusedRedBytes + fused_scale_bytes(M, K) + M * K <= kFusedLdsBytes;
+inline bool fused_fits(int64_t M, int64_t K) {
+  return M <= kFusedMaxM && kFusedRedBytes + fused_scale_bytes(M, K) + M * K <= kFusedLdsBytes;
 }
-inline bool decode_lds_fits(int64_t M, int64_t K) { return M <= kDecLdsMaxM && lds_fits(M, K); }
-inline bool fused_fits(int64_t M, int64_t K) { return M <= kFusedMaxM && lds_fits(M, K); }
 
-// QUANT: Xin is bf16 X [M, K] (sa unused); else Xin is e4m3 A [M, K] with
-// scales sa [M, K/128] (TS: one scale per tensor, sa[0] * sw[0])
-template <int kDepth, bool QUANT, bool TS>
+// X: bf16 [M, K]; P: K blocks packed per MFMA (M <= 16 / P)
+template <int kDepth, int P>
 __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(kDecWaves / 4, kDecWaves / 4)))
-void gemm_decode_lds_kernel(const void* __restrict__ Xin, const float* __restrict__ sa, const uint8_t* __restrict__ W,
-                            const float* __restrict__ sw, uint16_t* __restrict__ C, int M, int64_t N, int64_t K) {
-  static_assert(!(QUANT && TS), "the fused form takes block scales");
+void act_quant_gemm_decode_kernel(const uint16_t* __restrict__ X, const uint8_t* __restrict__ W,
+                                  const float* __restrict__ sw, uint16_t* __restrict__ C, int M, int64_t N,
+                                  int64_t K) {
+  constexpr int R = 16 / P;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kFusedLdsBytes];
   float4* red = reinterpret_cast<float4*>(lds);
   const int KB = static_cast<int>(K / kBK);
@@ -734,103 +776,89 @@ void gemm_decode_lds_kernel(const void* __restrict__ Xin, const float* __restric
   uint8_t* scode = lds + kFusedRedBytes + fused_scale_bytes(M, K);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * R;
 
-  const uint8_t* wp = W + (n0 + (lane & 15)) * K + 32 * (lane >> 4);
+  // lane l: W row n0 + rsub, K block P*s + grp of step s (as in the
+  // streaming kernel; a block past K contributes zeros)
+  const int rsub = (lane & 15) % R;
+  const int grp = (lane & 15) / R;
+  const uint8_t* wp = W + (n0 + rsub) * K + 32 * (lane >> 4);
   const float* swrow = sw + (n0 / 128) * KB;
-  const int nt = KB > wave ? (KB - wave + kDecWaves - 1) / kDecWaves : 0;
+  const int S = (KB + P - 1) / P;
+  const int nt = S > wave ? (S - wave + kDecWaves - 1) / kDecWaves : 0;
   uint4 wq[kDepth][2];
   auto loadw = [&](int d, int t) {
-    const int64_t kb = wave + static_cast<int64_t>(kDecWaves) * t;
-    wq[d][0] = *reinterpret_cast<const uint4*>(wp + kb * kBK);
-    wq[d][1] = *reinterpret_cast<const uint4*>(wp + kb * kBK + 16);
+    const int64_t kb = static_cast<int64_t>(wave + kDecWaves * t) * P + grp;
+    if (P == 1 || kb < KB) {
+      wq[d][0] = *reinterpret_cast<const uint4*>(wp + kb * kBK);
+      wq[d][1] = *reinterpret_cast<const uint4*>(wp + kb * kBK + 16);
+    } else {
+      wq[d][0] = wq[d][1] = make_uint4(0, 0, 0, 0);
+    }
   };
 #pragma unroll
   for (int d = 0; d < kDepth; ++d)
     if (d < nt) loadw(d, d);
 
-  // stage A in LDS; the loads of kPass passes are issued before any is used
+  // quantize X into LDS (row-major M x K, block b = m*KB + kb at element
+  // 128*b); the loads of kPass passes are issued before any is used
   constexpr int kPass = 4;
-  if constexpr (QUANT) {
-    // quantize X (row-major M x K, block b = m*KB + kb at element 128*b)
-    const uint16_t* X = static_cast<const uint16_t*>(Xin);
-    constexpr int kBlocksPerPass = 64 * kDecWaves / 8;
-    const int nblk = M * KB;
-    const int sub = threadIdx.x & 7;
-    for (int b0 = static_cast<int>(threadIdx.x >> 3); b0 < nblk; b0 += kPass * kBlocksPerPass) {
-      uint4 v[kPass][2];
+  constexpr int kBlocksPerPass = 64 * kDecWaves / 8;
+  const int nblk = M * KB;
+  const int sub = threadIdx.x & 7;
+  for (int b0 = static_cast<int>(threadIdx.x >> 3); b0 < nblk; b0 += kPass * kBlocksPerPass) {
+    uint4 v[kPass][2];
 #pragma unroll
-      for (int u = 0; u < kPass; ++u) {
-        const int b = b0 + u * kBlocksPerPass;
-        if (b < nblk) {
-          const uint4* xb = reinterpret_cast<const uint4*>(X + static_cast<int64_t>(b) * kBK);
-          v[u][0] = xb[sub];
-          v[u][1] = xb[8 + sub];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kPass; ++u) {
-        const int b = b0 + u * kBlocksPerPass;
-        if (b < nblk) {
-          uint2 o0, o1;
-          const float sb = quant_block_bf16(v[u][0], v[u][1], o0, o1);
-          const int m = b / KB, kb = b % KB;
-          // codes of elements 8*sub.. (quarter sub/4) and 64 + 8*sub..
-          // (quarter 2 + sub/4); both at byte 8*(sub%4) of their quarter
-          const int h = (sub & 3) >> 1;
-          uint8_t* cb = scode + static_cast<int64_t>(kb) * kBK * M + (sub & 1) * 8;
-          *reinterpret_cast<uint2*>(cb + ((h * 4 + (sub >> 2)) * M + m) * 16) = o0;
-          *reinterpret_cast<uint2*>(cb + ((h * 4 + 2 + (sub >> 2)) * M + m) * 16) = o1;
-          if (sub == 0) ssa[b] = sb;
-        }
+    for (int u = 0; u < kPass; ++u) {
+      const int b = b0 + u * kBlocksPerPass;
+      if (b < nblk) {
+        const uint4* xb = reinterpret_cast<const uint4*>(X + static_cast<int64_t>(b) * kBK);
+        v[u][0] = xb[sub];
+        v[u][1] = xb[8 + sub];
       }
     }
-  } else {
-    // copy the codes, 16 bytes a lane: chunk c = 2q + h of row m, block kb
-    const uint8_t* A = static_cast<const uint8_t*>(Xin);
-    const int nchunk = M * KB * 8;
-    for (int i0 = static_cast<int>(threadIdx.x); i0 < nchunk; i0 += kPass * 64 * kDecWaves) {
-      uint4 v[kPass];
 #pragma unroll
-      for (int u = 0; u < kPass; ++u) {
-        const int i = i0 + u * 64 * kDecWaves;
-        if (i < nchunk) v[u] = *reinterpret_cast<const uint4*>(A + static_cast<int64_t>(i) * 16);
-      }
-#pragma unroll
-      for (int u = 0; u < kPass; ++u) {
-        const int i = i0 + u * 64 * kDecWaves;
-        if (i < nchunk) {
-          const int m = i / (KB * 8), kb = (i / 8) % KB, c = i % 8;
-          *reinterpret_cast<uint4*>(scode + static_cast<int64_t>(kb) * kBK * M +
-                                    (((c & 1) * 4 + (c >> 1)) * M + m) * 16) = v[u];
-        }
+    for (int u = 0; u < kPass; ++u) {
+      const int b = b0 + u * kBlocksPerPass;
+      if (b < nblk) {
+        uint2 o0, o1;
+        const float sb = quant_block_bf16(v[u][0], v[u][1], o0, o1);
+        const int m = b / KB, kb = b % KB;
+        // codes of elements 8*sub.. (quarter sub/4) and 64 + 8*sub..
+        // (quarter 2 + sub/4); both at byte 8*(sub%4) of their quarter
+        const int h = (sub & 3) >> 1;
+        uint8_t* cb = scode + static_cast<int64_t>(kb) * kBK * M + (sub & 1) * 8;
+        *reinterpret_cast<uint2*>(cb + ((h * 4 + (sub >> 2)) * M + m) * 16) = o0;
+        *reinterpret_cast<uint2*>(cb + ((h * 4 + 2 + (sub >> 2)) * M + m) * 16) = o1;
+        if (sub == 0) ssa[b] = sb;
       }
     }
-    if constexpr (!TS)
-      for (int i = static_cast<int>(threadIdx.x); i < M * KB; i += 64 * kDecWaves) ssa[i] = sa[i];
   }
   __syncthreads();
 
-  // lane l: A row min(l%16, M-1) (rows past M repeat row M-1; their outputs
+  // lane l: A row min(rsub, M-1) (rows past M repeat row M-1; their outputs
   // are never stored), quarter l/16 of each K block
-  const int ar = min(lane & 15, M - 1);
+  const int ar = min(rsub, M - 1);
   const uint8_t* ap = scode + ((lane >> 4) * M + ar) * 16;
   const float* sp = ssa + ar * KB;
-  const float cst = TS ? sa[0] * sw[0] : 0.0f;
   v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   for (int t0 = 0; t0 < nt; t0 += kDepth) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
       const int t = t0 + d;
       if (t < nt) {
-        const int kb = wave + kDecWaves * t;
+        const int kb = (wave + kDecWaves * t) * P + grp;
+        const bool in = P == 1 || kb < KB;
         const v8i wf = v8i{(int)wq[d][0].x, (int)wq[d][0].y, (int)wq[d][0].z, (int)wq[d][0].w,
                            (int)wq[d][1].x, (int)wq[d][1].y, (int)wq[d][1].z, (int)wq[d][1].w};
         const uint8_t* ak = ap + static_cast<int64_t>(kb) * kBK * M;
-        const uint4 lo = *reinterpret_cast<const uint4*>(ak);
-        const uint4 hi = *reinterpret_cast<const uint4*>(ak + 4 * M * 16);
+        uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+        if (in) {
+          lo = *reinterpret_cast<const uint4*>(ak);
+          hi = *reinterpret_cast<const uint4*>(ak + 4 * M * 16);
+        }
         const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        const float cs = TS ? cst : sp[kb] * swrow[kb];
+        const float cs = in ? sp[kb] * swrow[kb] : 0.0f;
         if (t + kDepth < nt) loadw(d, t + kDepth);
         const v4f p = mfma_16x16x128_fp8(wf, af);
 #pragma unroll
@@ -839,33 +867,20 @@ void gemm_decode_lds_kernel(const void* __restrict__ Xin, const float* __restric
     }
   }
 
-  // the waves' partial sums, added in wave order (as in the streaming kernel)
   red[wave * 64 + lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
   __syncthreads();
-  const int t = threadIdx.x;
-  if (t < 64) {
-    const int m = t & 15;
-    if (m < M) {
-      float4 sum = red[t];
-#pragma unroll
-      for (int w = 1; w < kDecWaves; ++w) {
-        const float4 v = red[w * 64 + t];
-        sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
-      }
-      const int64_t n = n0 + 4 * (t >> 4);
-      uint2 o;
-      o.x = bf16x2_rne(sum.x, sum.y);
-      o.y = bf16x2_rne(sum.z, sum.w);
-      *reinterpret_cast<uint2*>(C + m * N + n) = o;
-    }
-  }
+  decode_store<P>(red, M, n0, N, C);
 }
 
-template <bool QUANT, bool TS>
-int launch_decode_lds(const void* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c, int64_t M,
-                      int64_t N, int64_t K, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_decode_lds_kernel<4, QUANT, TS>), dim3(static_cast<unsigned>(N / 16)),
-                     dim3(64 * kDecWaves), 0, st, a, sa, w, sw, c, static_cast<int>(M), N, K);
+int launch_act_quant_gemm_decode(const void* x, const uint8_t* w, const float* sw, uint16_t* c, int64_t M,
+                                 int64_t N, int64_t K, hipStream_t st) {
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  if (decode_pack(M) == 2)
+    hipLaunchKernelGGL((act_quant_gemm_decode_kernel<4, 2>), dim3(static_cast<unsigned>(N / 8)),
+                       dim3(64 * kDecWaves), 0, st, xb, w, sw, c, static_cast<int>(M), N, K);
+  else
+    hipLaunchKernelGGL((act_quant_gemm_decode_kernel<4, 1>), dim3(static_cast<unsigned>(N / 16)),
+                       dim3(64 * kDecWaves), 0, st, xb, w, sw, c, static_cast<int>(M), N, K);
   return FP8BS_OK;
 }
 
@@ -1124,9 +1139,7 @@ int gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m
   // decode shapes are bound by streaming W: the FMA kernels serve both scale
   // formats (with power-of-two scales the scale product is exact there too)
   if (use_decode(M)) {
-    if (decode_lds_fits(M, K))
-      rc = launch_decode_lds<false, MODE == 2>(a, a_scale, w, w_scale, c, M, N, K, st);
-    else if (M <= kDecStreamMaxM)
+    if (M <= kDecStreamMaxM)
       rc = launch_decode_stream<MODE == 2>(a, a_scale, w, w_scale, c, M, N, K, st);
     else
       rc = launch_decode<MODE == 2>(a, a_scale, w, w_scale, c, static_cast<float*>(workspace), M, N, K, st);
@@ -1210,8 +1223,8 @@ int fp8_act_quant_gemm_blockscaled(const void* x_bf16, const void* w_e4m3, const
     const DeviceInfo dev = current_device();
     if (dev.status != FP8BS_OK) return dev.status;
     (void)hipGetLastError();
-    launch_decode_lds<true, false>(x_bf16, nullptr, static_cast<const uint8_t*>(w_e4m3), w_scale,
-                                   static_cast<uint16_t*>(c_bf16), M, N, K, as_stream(stream));
+    launch_act_quant_gemm_decode(x_bf16, static_cast<const uint8_t*>(w_e4m3), w_scale,
+                                 static_cast<uint16_t*>(c_bf16), M, N, K, as_stream(stream));
     return launch_status();
   }
   // two launches through the workspace: block act-quant, then the GEMM

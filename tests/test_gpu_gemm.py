@@ -212,11 +212,11 @@ def test_bit_exact_against_matrix_core_model(dist):
                                    (3, 256, 128 * 7), (16, 128, 128 * 600), (40, 128, 128 * 500),
                                    (2, 128, 71424), (2, 128, 71552)])
 def test_decode_shapes(M, N, K):
-    # M <= 16: sixteen waves per 16 W rows, each taking every sixteenth K
-    # block, partial sums added in wave order (K = 7 blocks leaves waves
-    # without a block; K = 600 blocks runs many prefetch rounds per wave).
-    # For M <= 2 A is staged in LDS while it fits (2 x 71424 is the largest),
-    # else it is read from global memory per block (2 x 71552, M > 2).
+    # M <= 16: sixteen waves per workgroup, each taking every sixteenth step
+    # of K, partial sums added in a fixed order (K = 7 blocks leaves waves
+    # without a step; K = 600 blocks runs many prefetch rounds per wave).
+    # M <= 8 packs two K blocks into each MFMA (8 W rows per workgroup): an
+    # odd block count (1, 7, 559) leaves the last step half empty.
     # 16 < M <= 64: several K splits, fp32 partials in the workspace, reduced
     # in split order.
     rng = np.random.default_rng(M * 7 + N + K)
