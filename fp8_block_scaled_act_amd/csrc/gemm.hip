@@ -889,9 +889,11 @@ int launch_act_quant_gemm_decode(const void* x, const uint8_t* w, const float* s
 // that A is shared: workgroup (n tile of 64 rows, K split)
 // has four waves, wave w owning W rows 16w..16w+15 of the tile. Each wave
 // loads its W fragments straight from global memory into registers
-// (kDepth K blocks in flight), the K split's slice of A (at most 64 rows) is
-// staged once in LDS and shared, and each K block is one MFMA per 16
-// activation rows plus the scale FMAs. With more than one K split the fp32
+// (kDepth K blocks in flight), the K split's slice of A (at most 64 rows)
+// and its activation scales are staged once in LDS and shared, and each K
+// block is one MFMA per 16 activation rows plus the scale FMAs (reading the
+// scales from global memory in the K loop cost 2 us per call at M = 64 on
+// the decode shape: 15.9 against 13.9 us). With more than one K split the fp32
 // partial sums go to the workspace and a second kernel adds them in split
 // order (deterministic) and rounds to bf16.
 // ---------------------------------------------------------------------------
@@ -908,6 +910,7 @@ __global__ __launch_bounds__(256) void gemm_blockscaled_decode_kernel(
     const float* __restrict__ sw, uint16_t* __restrict__ C, float* __restrict__ ws, int M, int64_t N,
     int64_t K, int kb_per, int splits) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[KBMAX * MT * 16 * 128];
+  __shared__ float ssa[MT * 16 * KBMAX];     // the split's activation scales, [row][k]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kDecRows;
@@ -920,10 +923,6 @@ __global__ __launch_bounds__(256) void gemm_blockscaled_decode_kernel(
   const int64_t nrow = n0 + wave * 16 + (lane & 15);          // this lane's W row
   const uint8_t* wp = W + min<int64_t>(nrow, N - 1) * K + static_cast<int64_t>(kb0) * kBK + 32 * (lane >> 4);
   const float* swrow = sw + ((n0 + wave * 16) / 128) * KB + kb0;
-  int mrow[MT];
-#pragma unroll
-  for (int j = 0; j < MT; ++j) mrow[j] = min(j * 16 + (lane & 15), M - 1);
-
   // W fragments first: their HBM latency overlaps the staging of A
   uint4 wq[kDecDepth][2];
 #pragma unroll
@@ -946,6 +945,13 @@ __global__ __launch_bounds__(256) void gemm_blockscaled_decode_kernel(
     const uint4 v = *reinterpret_cast<const uint4*>(A + gr * K + static_cast<int64_t>(kb0 + kk) * kBK + c * 16);
     *reinterpret_cast<uint4*>(lds + (kk * MP + row) * 128 + ((c ^ swz(row)) << 4)) = v;
   }
+  // and the split's activation scales (rows >= M repeat row M-1), so that
+  // the K loop waits on no global load but W's
+  if constexpr (!TS)
+    for (int id = threadIdx.x; id < MP * nkb; id += 256) {
+      const int row = id / nkb, k = id - row * nkb;
+      ssa[row * KBMAX + k] = sa[static_cast<int64_t>(min(row, M - 1)) * KB + kb0 + k];
+    }
 
   __syncthreads();
 
@@ -969,7 +975,7 @@ __global__ __launch_bounds__(256) void gemm_blockscaled_decode_kernel(
         for (int j = 0; j < MT; ++j) {
           const v8i af = lds_frag(lds + k * MP * 128, j * 16 + (lane & 15), c0);
           const v4f p = mfma_16x16x128_fp8(wf, af);
-          const float cs = TS ? sa[0] * sw[0] : sa[static_cast<int64_t>(mrow[j]) * KB + kb0 + k] * swb;
+          const float cs = TS ? sa[0] * sw[0] : ssa[(j * 16 + (lane & 15)) * KBMAX + k] * swb;
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(p[r], cs, acc[j][r]);
         }
@@ -990,8 +996,13 @@ __global__ __launch_bounds__(256) void gemm_blockscaled_decode_kernel(
       o.y = bf16x2_rne(acc[j][2], acc[j][3]);
       *reinterpret_cast<uint2*>(C + m * N + n) = o;
     } else {
-      *reinterpret_cast<float4*>(ws + (static_cast<int64_t>(sp) * M + m) * N + n) =
-          make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+      // non-temporal: the partials are read once, by the reduce kernel (M = 64
+      // on the decode shape: 14.0 -> 13.0 us per call)
+      float* q = ws + (static_cast<int64_t>(sp) * M + m) * N + n;
+      __builtin_nontemporal_store(acc[j][0], q);
+      __builtin_nontemporal_store(acc[j][1], q + 1);
+      __builtin_nontemporal_store(acc[j][2], q + 2);
+      __builtin_nontemporal_store(acc[j][3], q + 3);
     }
   }
 }
