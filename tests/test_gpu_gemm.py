@@ -35,8 +35,9 @@ def run_gemm(qa, sa, qw, sw, label):
     return to_bf16_bits(c)
 
 
-def check_full(qa, sa, qw, sw, label):
-    c = run_gemm(qa, sa, qw, sw, label)
+def check_full(qa, sa, qw, sw, label, c=None):
+    if c is None:
+        c = run_gemm(qa, sa, qw, sw, label)
     R = gemm.gemm_blockscaled_ref(qa, sa, qw, sw)
     S = gemm.gemm_abs_ref(qa, sa, qw, sw)
     Se = gemm.gemm_exp_envelope_ref(qa, sa, qw, sw)
@@ -232,14 +233,18 @@ def test_gemm_workspace_size_and_reuse():
         assert fb.fp8_gemm_blockscaled_workspace_bytes(M, N, K) == 0
     M = 32
     wsb = fb.fp8_gemm_blockscaled_workspace_bytes(M, N, K)
-    assert wsb % (M * N * 4) == 0 and wsb >= M * N * 4
+    assert wsb >= M * N * 4 and wsb % (M * N * 4) == 0    # fp32 partials, one [M, N] per K split
     d = synth.gen_c3(M)
     qa, sa, qw, sw = operands(d["a"], d["w"])
     args = (u8_to_dev(qa), f32_to_dev(sa), u8_to_dev(qw), f32_to_dev(sw))
     ws = torch.full((wsb,), 0x7F, dtype=torch.uint8, device="cuda:0")     # garbage on entry
     c1 = fb.fp8_gemm_blockscaled(*args, workspace=ws)
     c2 = fb.fp8_gemm_blockscaled(*args, workspace=ws)
+    # other garbage: consecutive 64-bit integers
+    ws_seq = torch.arange(wsb // 8, dtype=torch.int64, device="cuda:0").view(torch.uint8)
+    c3 = fb.fp8_gemm_blockscaled(*args, workspace=ws_seq)
     torch.cuda.synchronize()
-    assert torch.equal(c1, c2)
+    assert torch.equal(c1, c2) and torch.equal(c1, c3)
+    check_full(qa, sa, qw, sw, "decode M=32 through a reused workspace", c=to_bf16_bits(c2))
     with pytest.raises(fb.Fp8bsError):
         fb.fp8_gemm_blockscaled(*args, workspace=ws[: wsb - 4])
