@@ -310,7 +310,7 @@ def fp8_act_quant_gemm_blockscaled_workspace_bytes(M: int, N: int, K: int) -> in
 def fp8_act_quant_gemm_blockscaled(x, w, w_scale, out=None, workspace=None):
     """C = A_q . W^T (bf16 [M, N]) where (A_q, a_scale) is the 1x128 block
     quantization of the bf16 activations x [M, K]; one kernel for decode
-    batches (M <= 4), else act-quant and GEMM through the workspace."""
+    batches (M <= 8), else act-quant and GEMM through the workspace."""
     _need(x, "x", torch.bfloat16)
     if w.dtype not in (E4M3, torch.uint8):
         raise TypeError("w must be float8_e4m3fn (or its uint8 bytes)")

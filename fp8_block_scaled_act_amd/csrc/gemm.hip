@@ -753,9 +753,10 @@ int launch_decode_stream(const uint8_t* a, const float* sa, const uint8_t* w, co
 // ---------------------------------------------------------------------------
 constexpr int kFusedLdsBytes = 160 * 1024;
 constexpr int kFusedRedBytes = kDecWaves * 64 * 16;
-// largest M for the one-kernel act-quant + GEMM: above it the two launches
-// are faster
-constexpr int64_t kFusedMaxM = 4;
+// largest M for the one-kernel act-quant + GEMM (N = 2048, K = 7168: one
+// kernel 5.6 / 6.2 / 8.5 us at M = 1 / 4 / 8 against 7.2 / 7.7 / 9.2 us
+// for the two launches)
+constexpr int64_t kFusedMaxM = 8;
 
 __host__ __device__ inline int64_t fused_scale_bytes(int64_t M, int64_t K) { return (M * (K / kBK) * 4 + 15) / 16 * 16; }
 inline bool fused_fits(int64_t M, int64_t K) {
@@ -786,28 +787,19 @@ void act_quant_gemm_decode_kernel(const uint16_t* __restrict__ X, const uint8_t*
   const float* swrow = sw + (n0 / 128) * KB;
   const int S = (KB + P - 1) / P;
   const int nt = S > wave ? (S - wave + kDecWaves - 1) / kDecWaves : 0;
-  uint4 wq[kDepth][2];
-  auto loadw = [&](int d, int t) {
-    const int64_t kb = static_cast<int64_t>(wave + kDecWaves * t) * P + grp;
-    if (P == 1 || kb < KB) {
-      wq[d][0] = *reinterpret_cast<const uint4*>(wp + kb * kBK);
-      wq[d][1] = *reinterpret_cast<const uint4*>(wp + kb * kBK + 16);
-    } else {
-      wq[d][0] = wq[d][1] = make_uint4(0, 0, 0, 0);
-    }
-  };
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d)
-    if (d < nt) loadw(d, d);
 
-  // quantize X into LDS (row-major M x K, block b = m*KB + kb at element
-  // 128*b); the loads of kPass passes are issued before any is used
+  // X is quantized into LDS (row-major M x K, block b = m*KB + kb at
+  // element 128*b), kPass blocks a thread per pass. The first pass's X loads
+  // are issued before the first W loads: loads complete in order, so X (in
+  // L2) issued after W (from HBM) could not be quantized before all of
+  // those W loads had landed.
   constexpr int kPass = 4;
   constexpr int kBlocksPerPass = 64 * kDecWaves / 8;
   const int nblk = M * KB;
   const int sub = threadIdx.x & 7;
-  for (int b0 = static_cast<int>(threadIdx.x >> 3); b0 < nblk; b0 += kPass * kBlocksPerPass) {
-    uint4 v[kPass][2];
+  const int bfirst = static_cast<int>(threadIdx.x >> 3);
+  uint4 v[kPass][2];
+  auto xload = [&](int b0) {
 #pragma unroll
     for (int u = 0; u < kPass; ++u) {
       const int b = b0 + u * kBlocksPerPass;
@@ -817,6 +809,8 @@ void act_quant_gemm_decode_kernel(const uint16_t* __restrict__ X, const uint8_t*
         v[u][1] = xb[8 + sub];
       }
     }
+  };
+  auto xquant = [&](int b0) {
 #pragma unroll
     for (int u = 0; u < kPass; ++u) {
       const int b = b0 + u * kBlocksPerPass;
@@ -833,6 +827,26 @@ void act_quant_gemm_decode_kernel(const uint16_t* __restrict__ X, const uint8_t*
         if (sub == 0) ssa[b] = sb;
       }
     }
+  };
+  xload(bfirst);
+
+  // W: the first kDepth steps of every wave are loaded unconditionally, so
+  // that the number of loads after X's is fixed and the wait for X does not
+  // include them. A block past K (or a step past the wave's last) reads
+  // the last block instead; the K loop zeroes or skips it.
+  uint4 wq[kDepth][2];
+  auto loadw = [&](int d, int t) {
+    const int64_t kb = min<int64_t>(static_cast<int64_t>(wave + kDecWaves * t) * P + grp, KB - 1);
+    wq[d][0] = *reinterpret_cast<const uint4*>(wp + kb * kBK);
+    wq[d][1] = *reinterpret_cast<const uint4*>(wp + kb * kBK + 16);
+  };
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) loadw(d, d);
+
+  xquant(bfirst);
+  for (int b0 = bfirst + kPass * kBlocksPerPass; b0 < nblk; b0 += kPass * kBlocksPerPass) {
+    xload(b0);
+    xquant(b0);
   }
   __syncthreads();
 
@@ -849,8 +863,9 @@ void act_quant_gemm_decode_kernel(const uint16_t* __restrict__ X, const uint8_t*
       if (t < nt) {
         const int kb = (wave + kDecWaves * t) * P + grp;
         const bool in = P == 1 || kb < KB;
-        const v8i wf = v8i{(int)wq[d][0].x, (int)wq[d][0].y, (int)wq[d][0].z, (int)wq[d][0].w,
-                           (int)wq[d][1].x, (int)wq[d][1].y, (int)wq[d][1].z, (int)wq[d][1].w};
+        v8i wf = v8i{(int)wq[d][0].x, (int)wq[d][0].y, (int)wq[d][0].z, (int)wq[d][0].w,
+                     (int)wq[d][1].x, (int)wq[d][1].y, (int)wq[d][1].z, (int)wq[d][1].w};
+        if (!in) wf = v8i{0, 0, 0, 0, 0, 0, 0, 0};
         const uint8_t* ak = ap + static_cast<int64_t>(kb) * kBK * M;
         uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
         if (in) {
@@ -874,12 +889,16 @@ void act_quant_gemm_decode_kernel(const uint16_t* __restrict__ X, const uint8_t*
 
 int launch_act_quant_gemm_decode(const void* x, const uint8_t* w, const float* sw, uint16_t* c, int64_t M,
                                  int64_t N, int64_t K, hipStream_t st) {
+  static_assert(kFusedMaxM <= kDecPackMaxM, "the fused form packs two K blocks per MFMA");
   const uint16_t* xb = static_cast<const uint16_t*>(x);
-  if (decode_pack(M) == 2)
-    hipLaunchKernelGGL((act_quant_gemm_decode_kernel<4, 2>), dim3(static_cast<unsigned>(N / 8)),
+  // the W loads of a wave's first kDepth steps are issued up front, whether
+  // or not the wave has that many: two when no wave has more (K <= 8192)
+  const int64_t steps = (K / kBK + 1) / 2;
+  if (steps <= 2 * kDecWaves)
+    hipLaunchKernelGGL((act_quant_gemm_decode_kernel<2, 2>), dim3(static_cast<unsigned>(N / 8)),
                        dim3(64 * kDecWaves), 0, st, xb, w, sw, c, static_cast<int>(M), N, K);
   else
-    hipLaunchKernelGGL((act_quant_gemm_decode_kernel<4, 1>), dim3(static_cast<unsigned>(N / 16)),
+    hipLaunchKernelGGL((act_quant_gemm_decode_kernel<4, 2>), dim3(static_cast<unsigned>(N / 8)),
                        dim3(64 * kDecWaves), 0, st, xb, w, sw, c, static_cast<int>(M), N, K);
   return FP8BS_OK;
 }
@@ -909,7 +928,9 @@ __global__ __launch_bounds__(256) void gemm_blockscaled_decode_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, uint16_t* __restrict__ C, float* __restrict__ ws, int M, int64_t N,
     int64_t K, int kb_per, int splits) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[KBMAX * MT * 16 * 128];
+  // the A slice, then a 16-byte slot that takes the stores of chunks past
+  // the slice's end
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[KBMAX * MT * 16 * 128 + 16];
   __shared__ float ssa[MT * 16 * KBMAX];     // the split's activation scales, [row][k]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -923,35 +944,78 @@ __global__ __launch_bounds__(256) void gemm_blockscaled_decode_kernel(
   const int64_t nrow = n0 + wave * 16 + (lane & 15);          // this lane's W row
   const uint8_t* wp = W + min<int64_t>(nrow, N - 1) * K + static_cast<int64_t>(kb0) * kBK + 32 * (lane >> 4);
   const float* swrow = sw + ((n0 + wave * 16) / 128) * KB + kb0;
-  // W fragments first: their HBM latency overlaps the staging of A
-  uint4 wq[kDecDepth][2];
+  // Stage A rows [0, 16*MT) x K blocks [kb0, kb0 + nkb) in LDS (rows >= M
+  // read row M-1: valid memory, results never stored), swizzled as in the
+  // tiled kernel, and the split's activation scales, so that the K loop
+  // waits on no global load but W's. The first pass of those loads (all of
+  // them while nkb * 16*MT * 8 <= kAPass * 256) is issued before the W
+  // loads: loads complete in order, so A (in L2) issued after W (from HBM)
+  // could not be stored before all of W had landed.
+  constexpr int MP = 16 * MT;
+  constexpr int kAPass = 8;
+  const int nchunk = nkb * MP * 8;
+  // chunk id: K block id / (8*MP), row (id / 8) % MP, 16-byte chunk id % 8;
+  // a load past the last chunk reads the last one again (unconditional
+  // loads leave the compiler no reason to wait for them early)
+  auto asrc = [&](int id) {
+    id = min(id, nchunk - 1);
+    const int64_t gr = min((id / 8) % MP, M - 1);
+    return reinterpret_cast<const uint4*>(A + gr * K + static_cast<int64_t>(kb0 + id / (MP * 8)) * kBK + (id % 8) * 16);
+  };
+  auto adst = [&](int id) {
+    const int row = (id / 8) % MP;
+    return reinterpret_cast<uint4*>(id < nchunk ? lds + ((id / (MP * 8)) * MP + row) * 128 + (((id % 8) ^ swz(row)) << 4)
+                                                : lds + KBMAX * MT * 16 * 128);
+  };
+  const int id0 = static_cast<int>(threadIdx.x);
+  // (eight named registers rather than an array, which the compiler would
+  // keep in scratch memory)
+#define FP8BS_ALOAD(u) const uint4 av##u = *asrc(id0 + (u) * 256);
+  FP8BS_ALOAD(0) FP8BS_ALOAD(1) FP8BS_ALOAD(2) FP8BS_ALOAD(3)
+  FP8BS_ALOAD(4) FP8BS_ALOAD(5) FP8BS_ALOAD(6) FP8BS_ALOAD(7)
+#undef FP8BS_ALOAD
+  static_assert(kAPass == 8, "one named register per chunk of the first pass");
+  // the first pass of the scales: MP * nkb <= 16 * MT * KBMAX values
+  constexpr int kSPass = (MT * 16 * KBMAX + 255) / 256;
+  float sv[kSPass];
+  if constexpr (!TS) {
 #pragma unroll
-  for (int d = 0; d < kDecDepth; ++d) {
-    if (d < nkb) {
-      wq[d][0] = *reinterpret_cast<const uint4*>(wp + d * kBK);
-      wq[d][1] = *reinterpret_cast<const uint4*>(wp + d * kBK + 16);
+    for (int u = 0; u < kSPass; ++u) {
+      const int id = min(static_cast<int>(threadIdx.x) + u * 256, MP * nkb - 1);
+      const int row = id / nkb, k = id - row * nkb;
+      sv[u] = sa[static_cast<int64_t>(min(row, M - 1)) * KB + kb0 + k];
     }
   }
 
-  // stage A rows [0, 16*MT) x K blocks [kb0, kb0 + nkb) in LDS (rows >= M
-  // read row M-1: valid memory, results never stored), swizzled as in the
-  // tiled kernel
-  constexpr int MP = 16 * MT;
-  for (int id = threadIdx.x; id < nkb * MP * 8; id += 256) {
-    const int kk = id / (MP * 8);
-    const int row = (id / 8) % MP;
-    const int c = id % 8;
-    const int64_t gr = min(row, M - 1);
-    const uint4 v = *reinterpret_cast<const uint4*>(A + gr * K + static_cast<int64_t>(kb0 + kk) * kBK + c * 16);
-    *reinterpret_cast<uint4*>(lds + (kk * MP + row) * 128 + ((c ^ swz(row)) << 4)) = v;
+  // W fragments: the first kDecDepth blocks, loaded unconditionally (a block
+  // past the split's last reads its last block and is never used), so that
+  // the number of loads after A's is fixed; the scheduling barriers keep
+  // the compiler from moving A's loads behind them
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 wq[kDecDepth][2];
+#pragma unroll
+  for (int d = 0; d < kDecDepth; ++d) {
+    const int kk = min(d, nkb - 1);
+    wq[d][0] = *reinterpret_cast<const uint4*>(wp + kk * kBK);
+    wq[d][1] = *reinterpret_cast<const uint4*>(wp + kk * kBK + 16);
   }
-  // and the split's activation scales (rows >= M repeat row M-1), so that
-  // the K loop waits on no global load but W's
-  if constexpr (!TS)
-    for (int id = threadIdx.x; id < MP * nkb; id += 256) {
-      const int row = id / nkb, k = id - row * nkb;
-      ssa[row * KBMAX + k] = sa[static_cast<int64_t>(min(row, M - 1)) * KB + kb0 + k];
+
+  __builtin_amdgcn_sched_barrier(0);
+#define FP8BS_ASTORE(u) *adst(id0 + (u) * 256) = av##u;
+  FP8BS_ASTORE(0) FP8BS_ASTORE(1) FP8BS_ASTORE(2) FP8BS_ASTORE(3)
+  FP8BS_ASTORE(4) FP8BS_ASTORE(5) FP8BS_ASTORE(6) FP8BS_ASTORE(7)
+#undef FP8BS_ASTORE
+  if constexpr (!TS) {
+#pragma unroll
+    for (int u = 0; u < kSPass; ++u) {
+      const int id = static_cast<int>(threadIdx.x) + u * 256;
+      if (id < MP * nkb) {
+        const int row = id / nkb, k = id - row * nkb;
+        ssa[row * KBMAX + k] = sv[u];
+      }
     }
+  }
+  for (int id = id0 + kAPass * 256; id < nchunk; id += 256) *adst(id) = *asrc(id);
 
   __syncthreads();
 

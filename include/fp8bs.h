@@ -229,8 +229,8 @@ int fp8_act_quant_block_tensor(const void* x_bf16, int64_t M, int64_t K,
  * The DeepSeek-V3 page ("How to Profile DeepSeek-V3 Inference Kernels Using
  * Triton Autotuning", section "Analyzing FP8 Quantization Sensitivity" and
  * the FAQ entry on profiling act_quant_kernel separately) notes that the
- * activation quantization can dominate at small batch sizes. For M <= 4
- * (and M*K + M*K/32 <= 144 KiB, e.g. K <= 35712 at M = 4) this is ONE kernel:
+ * activation quantization can dominate at small batch sizes. For M <= 8
+ * (and M*K + M*K/32 <= 144 KiB, e.g. K <= 17792 at M = 8) this is ONE kernel:
  * every workgroup quantizes x into LDS and runs the decode GEMM from there,
  * with no workspace and no quantized copy of x in global memory; C is then
  * bit-for-bit the two-call result. Otherwise the call enqueues the two steps

@@ -154,11 +154,12 @@ def test_act_quant_gemm_argument_errors(L):
     assert f(P, P, P, P, 4, 128, 130, None, 0, None) == ESHAPE
     assert f(PU, P, P, P, 4, 128, 128, None, 0, None) == EALIGN
     assert f(P, P, P, PU, 4, 128, 128, None, 0, None) == EALIGN
-    # one kernel (no workspace) for M <= 4 while x's codes and scales fit in LDS
-    assert ws(1, 2048, 7168) == 0 and ws(4, 2048, 7168) == 0 and ws(4, 2048, 35712) == 0
+    # one kernel (no workspace) for M <= 8 while x's codes and scales fit in LDS
+    assert ws(1, 2048, 7168) == 0 and ws(4, 2048, 35712) == 0 and ws(8, 2048, 7168) == 0
+    assert ws(8, 2048, 17792) == 0
     # otherwise act-quant and GEMM through the workspace: codes, scales, GEMM workspace
     assert ws(4, 2048, 35840) == 4 * 35840 + 4608
-    assert ws(8, 2048, 7168) == 8 * 7168 + 1792
+    assert ws(9, 2048, 7168) == 9 * 7168 + 2048
     assert ws(8, 2048, 17920) == 8 * 17920 + 4608
     assert ws(16, 2048, 7168) == 16 * 7168 + 3584
     assert ws(64, 2048, 7168) == 64 * 7168 + 14336 + L.fp8_gemm_blockscaled_workspace_bytes(64, 2048, 7168)

@@ -3,7 +3,7 @@
 
 The oracle quantizes x with the 1x128 block rule and multiplies in fp64; the
 comparison rule is the GEMM's (oracle.gemm.compare_gemm). Where the call runs
-as one kernel (M <= 4, x's codes in LDS) its output must also equal, bit for
+as one kernel (M <= 8, x's codes in LDS) its output must also equal, bit for
 bit, the two-call path on the GPU (fp8_act_quant_block, then
 fp8_gemm_blockscaled), which performs the same operations in the same order.
 """
@@ -50,10 +50,10 @@ def check_oracle(c, x_bits, qw, sw, label):
     assert res["ok"], (label, res)
 
 
-@pytest.mark.parametrize("M", [1, 2, 4, 5, 8, 16])
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 8, 9, 16])
 def test_decode_workload(M):
     # the decode workload's shapes and distributions (N=2048, K=7168); one
-    # kernel up to M = 4, two launches from M = 5
+    # kernel up to M = 8, two launches from M = 9
     d = synth.gen_c3(M)
     qw, sw = quant.weight_quant_block(d["w"])
     c = run_fused(d["a"], qw, sw, f"C3 M={M}")
@@ -62,12 +62,16 @@ def test_decode_workload(M):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (3, 256, 384), (4, 384, 35712), (3, 640, 128 * 7),
-                                   (4, 128, 35840), (7, 640, 2560), (8, 384, 17792), (9, 256, 1024),
-                                   (40, 384, 2048), (64, 2048, 7168), (300, 512, 1024)])
+                                   (4, 128, 35840), (7, 640, 2560), (8, 384, 17792), (8, 128, 17920),
+                                   (5, 256, 128 * 200), (2, 256, 128 * 301), (9, 256, 1024), (40, 384, 2048),
+                                   (64, 2048, 7168),
+                                   (300, 512, 1024)])
 def test_shapes(M, N, K):
-    # (4, 384, 35712): largest K that runs as one kernel at M = 4; K = 7
-    # blocks leaves the last pair of packed K blocks half empty;
-    # (4, 128, 35840) and M > 4: act-quant and GEMM through the workspace
+    # (4, 384, 35712) and (8, 384, 17792): largest K that runs as one kernel
+    # at M = 4 and 8; K = 7 blocks leaves the last pair of packed K blocks
+    # half empty; K = 200 and 301 blocks take four steps in flight per wave;
+    # (4, 128, 35840), (8, 128, 17920) and M > 8: act-quant and GEMM through
+    # the workspace
     rng = np.random.default_rng(M * 7 + N + K)
     x = synth.f64_to_bf16_bits(rng.standard_t(3.0, size=(M, K)))
     qw, sw = weights(rng, N, K)
