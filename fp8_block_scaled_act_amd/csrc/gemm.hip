@@ -736,11 +736,11 @@ int launch_decode_stream(const uint8_t* a, const float* sa, const uint8_t* w, co
 //
 // Same workgroup shape, K order and packing as the streaming kernel above:
 // R W rows per workgroup over the whole of K, wave w taking steps w, w+16,
-// ... of P K blocks each. Each workgroup first issues its waves' first W
-// loads, then quantizes all of X into LDS (codes and scales) while those
-// loads are in flight, with the act-quant kernel's rule and lane mapping
-// (eight lanes per 1x128 block, the same helper), and runs the K loop with
-// A fragments and scales read from LDS. The arithmetic after that is the
+// ... of P K blocks each. Each workgroup quantizes all of X into LDS (codes
+// and scales) while its waves' first W loads are in flight, with the
+// act-quant kernel's rule and lane mapping (eight lanes per 1x128 block, the
+// same helper), and runs the K loop with A fragments and scales read from
+// LDS (the order of the loads is explained below). The arithmetic after that is the
 // streaming kernel's, operation for operation, so the results are those of
 // the two-launch path (act-quant, then the GEMM) bit for bit. Every
 // workgroup quantizes all of X: that redundant work grows with M, so the
