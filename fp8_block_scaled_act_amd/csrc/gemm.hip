@@ -605,9 +605,8 @@ __device__ __forceinline__ float row16_sum(float v) {
 // both shifted by g*R). A row of 16 threads takes one output group: thread
 // i adds the P group terms of wave i in group order, then the row adds the
 // waves by lane swaps. The order is fixed, so the result is deterministic.
-template <int P>
+template <int P, int R = 16 / P>
 __device__ __forceinline__ void decode_store(const float4* red, int M, int64_t n0, int64_t N, uint16_t* C) {
-  constexpr int R = 16 / P;
   static_assert(kDecWaves <= 16, "one wave per thread of a 16-thread row");
   const int nout = (R / 4) * M;
   const int i = threadIdx.x & 15;
@@ -638,13 +637,17 @@ __device__ __forceinline__ void decode_store(const float4* red, int M, int64_t n
 }
 
 // P: K blocks packed per MFMA (M <= 16 / P); kDecDepth: steps in flight per
-// wave; TS: one scale per tensor (sa[0] * sw[0] for every block)
-template <int P, int kDecDepth, bool TS>
+// wave; TS: one scale per tensor (sa[0] * sw[0] for every block); HALF (with
+// P = 1, for 8 < M <= 16): 8 W rows per workgroup, so that every CU streams
+// W here too, the MFMA's rows 8..15 carrying zeros (N = 2048, K = 7168:
+// 8.8 / 9.7 / 10.7 -> 7.7 / 8.6 / 9.5 us at M = 9 / 12 / 16)
+template <int P, int kDecDepth, bool TS, bool HALF = false>
 __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(kDecWaves / 4, kDecWaves / 4)))
 void gemm_blockscaled_decode_stream_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, uint16_t* __restrict__ C, int M, int64_t N, int64_t K) {
-  constexpr int R = 16 / P;
+  static_assert(!HALF || P == 1, "half tiles take one K block per step");
+  constexpr int R = HALF ? 8 : 16 / P;
   __shared__ float4 red[kDecWaves * 64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -653,12 +656,14 @@ void gemm_blockscaled_decode_stream_kernel(
 
   // lane l supplies W row n0 + rsub and A row rsub (rows past M read row
   // M-1: valid memory, results never stored) of K block P*s + grp of step s,
-  // bytes 32*(l/16) ..+32 of the block
-  const int rsub = (lane & 15) % R;
-  const int grp = (lane & 15) / R;
+  // bytes 32*(l/16) ..+32 of the block; HALF: W row n0 + l%8 from lanes with
+  // l%16 < 8 (zeros from the others), A row l%16
+  const int rsub = HALF ? (lane & 7) : (lane & 15) % R;
+  const int grp = HALF ? 0 : (lane & 15) / R;
+  const bool wuse = !HALF || (lane & 15) < 8;
   const int koff = 32 * (lane >> 4);
   const uint8_t* wp = W + (n0 + rsub) * K + koff;
-  const int64_t am = min(rsub, M - 1);
+  const int64_t am = min(HALF ? (lane & 15) : rsub, M - 1);
   const uint8_t* ap = A + am * K + koff;
   const float* sp = sa + am * KB;
   const float* swrow = sw + (n0 / 128) * KB;
@@ -674,8 +679,12 @@ void gemm_blockscaled_decode_stream_kernel(
   auto load = [&](int d, int t) {
     const int64_t kb = static_cast<int64_t>(wave + kDecWaves * t) * P + grp;
     if (P == 1 || kb < KB) {
-      wq[d][0] = *reinterpret_cast<const uint4*>(wp + kb * kBK);
-      wq[d][1] = *reinterpret_cast<const uint4*>(wp + kb * kBK + 16);
+      if (wuse) {
+        wq[d][0] = *reinterpret_cast<const uint4*>(wp + kb * kBK);
+        wq[d][1] = *reinterpret_cast<const uint4*>(wp + kb * kBK + 16);
+      } else {
+        wq[d][0] = wq[d][1] = make_uint4(0, 0, 0, 0);
+      }
       aq[d][0] = *reinterpret_cast<const uint4*>(ap + kb * kBK);
       aq[d][1] = *reinterpret_cast<const uint4*>(ap + kb * kBK + 16);
       if constexpr (!TS) sq[d] = sp[kb];
@@ -713,7 +722,7 @@ void gemm_blockscaled_decode_stream_kernel(
 
   red[wave * 64 + lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
   __syncthreads();
-  decode_store<P>(red, M, n0, N, C);
+  decode_store<P, R>(red, M, n0, N, C);
 }
 
 template <bool TS>
@@ -723,7 +732,7 @@ int launch_decode_stream(const uint8_t* a, const float* sa, const uint8_t* w, co
     hipLaunchKernelGGL((gemm_blockscaled_decode_stream_kernel<2, 4, TS>), dim3(static_cast<unsigned>(N / 8)),
                        dim3(64 * kDecWaves), 0, st, a, sa, w, sw, c, static_cast<int>(M), N, K);
   else
-    hipLaunchKernelGGL((gemm_blockscaled_decode_stream_kernel<1, 4, TS>), dim3(static_cast<unsigned>(N / 16)),
+    hipLaunchKernelGGL((gemm_blockscaled_decode_stream_kernel<1, 4, TS, true>), dim3(static_cast<unsigned>(N / 8)),
                        dim3(64 * kDecWaves), 0, st, a, sa, w, sw, c, static_cast<int>(M), N, K);
   return FP8BS_OK;
 }

@@ -211,13 +211,14 @@ def test_bit_exact_against_matrix_core_model(dist):
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (5, 256, 1024), (16, 2048, 7168), (17, 384, 2048),
                                    (33, 640, 4096), (64, 2048, 7168), (64, 128, 128 * 40), (48, 7168, 2048),
                                    (3, 256, 128 * 7), (16, 128, 128 * 600), (40, 128, 128 * 500),
-                                   (2, 128, 71424), (2, 128, 71552)])
+                                   (2, 128, 71424), (2, 128, 71552), (13, 384, 128 * 9), (9, 128, 128)])
 def test_decode_shapes(M, N, K):
     # M <= 16: sixteen waves per workgroup, each taking every sixteenth step
     # of K, partial sums added in a fixed order (K = 7 blocks leaves waves
     # without a step; K = 600 blocks runs many prefetch rounds per wave).
     # M <= 8 packs two K blocks into each MFMA (8 W rows per workgroup): an
-    # odd block count (1, 7, 559) leaves the last step half empty.
+    # odd block count (1, 7, 559) leaves the last step half empty. 8 < M <= 16
+    # takes 8 W rows per workgroup too, the MFMA's other 8 rows zero.
     # 16 < M <= 64: several K splits, fp32 partials in the workspace, reduced
     # in split order.
     rng = np.random.default_rng(M * 7 + N + K)
