@@ -240,11 +240,23 @@ __device__ __forceinline__ void store_nt(uint2 v, uint2* p) {
 // walked it from the start, so the last-level cache holds its most recently
 // read part, which this pass then reads first (when the input is larger
 // than that cache, a walk in the same order would find every line evicted)
+// pre: the first iteration's vectors, loaded by the caller (each index
+// clamped to the tensor, so the loads are unconditional); used only where
+// that iteration is a full one
 template <bool kFast>
 __device__ __forceinline__ void quant_range_nt(const uint4* xv, uint2* qv, int64_t nvec,
                                                 int64_t first, int64_t stride, float s, float r,
-                                                bool zero) {
+                                                bool zero, const uint4 (&pre)[kVecPerThread]) {
   int64_t i = first;
+  if (i + (kVecPerThread - 1) * stride < nvec) {
+#pragma unroll
+    for (int j = 0; j < kVecPerThread; ++j) {
+      uint2 o = quant8<kFast>(pre[j], s, r);
+      if (zero) o = make_uint2(0u, 0u);
+      store_nt(o, qv + nvec - 1 - (i + j * stride));
+    }
+    i += kVecPerThread * stride;
+  }
   for (; i + (kVecPerThread - 1) * stride < nvec; i += kVecPerThread * stride) {
     uint4 v[kVecPerThread];
 #pragma unroll
@@ -325,23 +337,35 @@ __global__ __launch_bounds__(kThreads) void tensor_apply_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ q, float* __restrict__ scale,
     const float* __restrict__ partial, int npartial, int64_t numel) {
   __shared__ float lds[kThreads / 64];
-  float m = 0.0f;
-  for (int i = threadIdx.x; i < npartial; i += kThreads) m = fmaxf(m, partial[i]);
-  const float amax = block_max<kThreads>(m, lds);
-  const float s = div_ieee(amax, kE4m3Max);
-  const bool zero = amax == 0.0f;
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint2* qv = reinterpret_cast<uint2*>(q);
   const int64_t nvec = numel >> 3;
   const int64_t first = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  // The first iteration's vectors go out before the partial maxima are read,
+  // so that their latency overlaps the reduction of the partials (which the
+  // quantization needs first). Unconditional loads at clamped indices: a
+  // conditional one would be sunk by the compiler to its use, after the
+  // partials.
+  uint4 pre[kVecPerThread];
+#pragma unroll
+  for (int j = 0; j < kVecPerThread; ++j) {
+    const int64_t idx = nvec - 1 - (first + j * stride);
+    pre[j] = xv[idx > 0 ? idx : 0];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < npartial; i += kThreads) m = fmaxf(m, partial[i]);
+  const float amax = block_max<kThreads>(m, lds);
+  const float s = div_ieee(amax, kE4m3Max);
+  const bool zero = amax == 0.0f;
   const bool head = blockIdx.x == 0 && threadIdx.x == 0;
   if (s >= kFastScaleMin) {
     const float r = div_ieee(1.0f, s);
-    quant_range_nt<true>(xv, qv, nvec, first, stride, s, r, zero);
+    quant_range_nt<true>(xv, qv, nvec, first, stride, s, r, zero, pre);
     if (head) tail_quant<true>(x, q, nvec << 3, numel, s, r, zero);
   } else {
-    quant_range_nt<false>(xv, qv, nvec, first, stride, s, 0.0f, zero);
+    quant_range_nt<false>(xv, qv, nvec, first, stride, s, 0.0f, zero, pre);
     if (head) tail_quant<false>(x, q, nvec << 3, numel, s, 0.0f, zero);
   }
   if (head) scale[0] = s;
