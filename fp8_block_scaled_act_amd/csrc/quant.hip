@@ -240,23 +240,23 @@ __device__ __forceinline__ void store_nt(uint2 v, uint2* p) {
 // walked it from the start, so the last-level cache holds its most recently
 // read part, which this pass then reads first (when the input is larger
 // than that cache, a walk in the same order would find every line evicted)
-// pre: the first iteration's vectors, loaded by the caller (each index
-// clamped to the tensor, so the loads are unconditional); used only where
-// that iteration is a full one
+// pre: the thread's first kVecPerThread vectors (i = first + j*stride),
+// loaded by the caller (each index clamped to the tensor, so the loads are
+// unconditional); those past the end are not stored
 template <bool kFast>
 __device__ __forceinline__ void quant_range_nt(const uint4* xv, uint2* qv, int64_t nvec,
                                                 int64_t first, int64_t stride, float s, float r,
                                                 bool zero, const uint4 (&pre)[kVecPerThread]) {
-  int64_t i = first;
-  if (i + (kVecPerThread - 1) * stride < nvec) {
 #pragma unroll
-    for (int j = 0; j < kVecPerThread; ++j) {
+  for (int j = 0; j < kVecPerThread; ++j) {
+    const int64_t i = first + j * stride;
+    if (i < nvec) {
       uint2 o = quant8<kFast>(pre[j], s, r);
       if (zero) o = make_uint2(0u, 0u);
-      store_nt(o, qv + nvec - 1 - (i + j * stride));
+      store_nt(o, qv + nvec - 1 - i);
     }
-    i += kVecPerThread * stride;
   }
+  int64_t i = first + kVecPerThread * stride;
   for (; i + (kVecPerThread - 1) * stride < nvec; i += kVecPerThread * stride) {
     uint4 v[kVecPerThread];
 #pragma unroll
