@@ -249,3 +249,17 @@ def test_gemm_workspace_size_and_reuse():
     check_full(qa, sa, qw, sw, "decode M=32 through a reused workspace", c=to_bf16_bits(c2))
     with pytest.raises(fb.Fp8bsError):
         fb.fp8_gemm_blockscaled(*args, workspace=ws[: wsb - 4])
+
+
+@pytest.mark.parametrize("M", [1, 5, 8, 12, 16, 40])
+def test_decode_paths_are_deterministic(M):
+    # the decode kernels add their partial sums in a fixed order (waves, K
+    # block groups, K splits), so repeated calls give identical bits
+    fb = binding()
+    d = synth.gen_c3(M)
+    qa, sa, qw, sw = operands(d["a"], d["w"])
+    args = (u8_to_dev(qa), f32_to_dev(sa), u8_to_dev(qw), f32_to_dev(sw))
+    say("decode determinism", M)
+    outs = [fb.fp8_gemm_blockscaled(*args) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:]), M
