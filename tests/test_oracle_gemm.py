@@ -164,24 +164,6 @@ def test_exp_envelope_closed_form():
     assert env[0x7E] == 256.0 and env[0x38] == 1.0
 
 
-def test_rows_sampler_matches_full():
-    rng = np.random.default_rng(7)
-    M, N, K = 6, 256, 256
-    qa, qw = rand_codes(rng, (M, K)), rand_codes(rng, (N, K))
-    sa = rng.uniform(0.1, 2, size=(M, K // 128)).astype(np.float32)
-    sw = rng.uniform(0.1, 2, size=(N // 128, K // 128)).astype(np.float32)
-    R = gemm.gemm_blockscaled_ref(qa, sa, qw, sw)
-    S = gemm.gemm_abs_ref(qa, sa, qw, sw)
-    rows = np.array([0, 5, 3, 3]); cols = np.array([255, 0, 128, 127])
-    Se = gemm.gemm_exp_envelope_ref(qa, sa, qw, sw)
-    r, s, se = gemm.gemm_rows_ref(qa, sa, qw, sw, rows, cols)
-    # same sums in another order: equal up to fp64 summation error
-    assert np.all(np.abs(r - R[rows, cols]) <= K * 2.0 ** -52 * S[rows, cols])
-    assert np.all(np.abs(s - S[rows, cols]) <= K * 2.0 ** -52 * S[rows, cols])
-    assert np.all(np.abs(se - Se[rows, cols]) <= K * 2.0 ** -52 * Se[rows, cols])
-
-
-
 def test_tensorscaled_ref_is_block_ref_with_constant_blocks():
     rng = np.random.default_rng(51)
     M, N, K = 9, 256, 384
