@@ -45,13 +45,12 @@ __all__ = [
     "fp8_act_quant_block_tensor_workspace_bytes",
     "fp8_act_quant_block_tensor",
     "debug_encode_e4m3",
+    "debug_mfma_block",
     "EXPORTED_SYMBOLS",
 ]
 
-# FP8BS_LIB may point at another build of the same library (e.g. to compare
-# kernel variants); by default the library built in this package directory.
-LIB_PATH = os.environ.get("FP8BS_LIB") or os.path.join(
-    os.path.dirname(os.path.abspath(__file__)), "libfp8bs.so")
+# the library built in this package directory (fp8_block_scaled_act_amd.build)
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8bs.so")
 
 EXPORTED_SYMBOLS = (
     "fp8bs_status_string",
@@ -71,6 +70,7 @@ EXPORTED_SYMBOLS = (
     "fp8_act_quant_block_tensor_workspace_bytes",
     "fp8_act_quant_block_tensor",
     "fp8bs_debug_encode_e4m3",
+    "fp8bs_debug_mfma_block",
 )
 
 E4M3 = torch.float8_e4m3fn
@@ -132,6 +132,8 @@ def lib() -> ctypes.CDLL:
     L.fp8_act_quant_block_tensor.restype = ctypes.c_int
     L.fp8bs_debug_encode_e4m3.argtypes = [fp, vp, i64, vp]
     L.fp8bs_debug_encode_e4m3.restype = ctypes.c_int
+    L.fp8bs_debug_mfma_block.argtypes = [vp, vp, fp, i64, vp]
+    L.fp8bs_debug_mfma_block.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -158,6 +160,46 @@ def _need(t: torch.Tensor, name: str, dtype, device=None):
         raise ValueError(f"{name} must be contiguous (strided views are not supported)")
 
 
+def _out(t, name: str, dtypes, shape, device):
+    """A caller-supplied output: a contiguous tensor of one of ``dtypes``, of
+    exactly ``shape``, on ``device`` (the kernels write all of it)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be one of {dtypes}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+_CODES = (E4M3, torch.uint8)
+_F32 = (torch.float32,)
+_BF16 = (torch.bfloat16,)
+
+
+def _workspace(ws, need: int, device):
+    """The workspace to pass: the caller's (a contiguous tensor on
+    ``device``; its size in bytes is what the library is told) or a new one
+    of ``need`` bytes; None when no workspace is needed and none was given."""
+    if ws is None:
+        return torch.empty((need,), dtype=torch.uint8, device=device) if need > 0 else None
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if ws.device != device:
+        raise ValueError(f"workspace is on {ws.device}, expected {device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return ws
+
+
+def _nbytes(ws) -> int:
+    return ws.numel() * ws.element_size() if ws is not None else 0
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
@@ -167,11 +209,14 @@ def _act_quant(fn: str, x: torch.Tensor, out, dtype=torch.bfloat16):
     if x.dim() != 2:
         raise ValueError("x must be 2-D [M, K]")
     M, K = x.shape
+    sshape = (M, K // 128 if K % 128 == 0 else 1)
     if out is None:
         q = torch.empty((M, K), dtype=E4M3, device=x.device)
-        s = torch.empty((M, K // 128 if K % 128 == 0 else 1), dtype=torch.float32, device=x.device)
+        s = torch.empty(sshape, dtype=torch.float32, device=x.device)
     else:
         q, s = out
+        _out(q, "q", _CODES, (M, K), x.device)
+        _out(s, "scale", _F32, sshape, x.device)
     with torch.cuda.device(x.device):
         rc = getattr(lib(), fn)(_ptr(x), M, K, _ptr(q), _ptr(s), ctypes.c_void_p(_stream(x.device)))
     _check(fn, rc)
@@ -206,13 +251,14 @@ def fp8_amax_quant_tensor(x: torch.Tensor, out=None, workspace=None):
         s = torch.empty((1,), dtype=torch.float32, device=x.device)
     else:
         q, s = out
+        _out(q, "q", _CODES, x.shape, x.device)
+        _out(s, "scale", _F32, (1,), x.device)
     wsb = fp8_amax_quant_tensor_workspace_bytes(numel) if numel > 0 else 0
-    if workspace is None and wsb > 0:
-        workspace = torch.empty((wsb,), dtype=torch.uint8, device=x.device)
+    workspace = _workspace(workspace, wsb, x.device)
     with torch.cuda.device(x.device):
         rc = lib().fp8_amax_quant_tensor(
-            _ptr(x), numel, _ptr(q), _ptr(s), _ptr(workspace),
-            workspace.numel() if workspace is not None else 0, ctypes.c_void_p(_stream(x.device)))
+            _ptr(x), numel, _ptr(q), _ptr(s), _ptr(workspace), _nbytes(workspace),
+            ctypes.c_void_p(_stream(x.device)))
     _check("fp8_amax_quant_tensor", rc)
     return q, s
 
@@ -229,21 +275,24 @@ def fp8_act_quant_block_tensor(x: torch.Tensor, out=None, workspace=None):
     if x.dim() != 2:
         raise ValueError("x must be 2-D [M, K]")
     M, K = x.shape
+    sshape = (M, K // 128 if K % 128 == 0 else 1)
     if out is None:
         qb = torch.empty((M, K), dtype=E4M3, device=x.device)
-        sb = torch.empty((M, K // 128 if K % 128 == 0 else 1), dtype=torch.float32, device=x.device)
+        sb = torch.empty(sshape, dtype=torch.float32, device=x.device)
         qt = torch.empty((M, K), dtype=E4M3, device=x.device)
         st = torch.empty((1,), dtype=torch.float32, device=x.device)
     else:
         qb, sb, qt, st = out
+        _out(qb, "q_block", _CODES, (M, K), x.device)
+        _out(sb, "block_scale", _F32, sshape, x.device)
+        _out(qt, "q_tensor", _CODES, (M, K), x.device)
+        _out(st, "tensor_scale", _F32, (1,), x.device)
     wsb = fp8_act_quant_block_tensor_workspace_bytes(M, K)
-    if workspace is None and wsb > 0:
-        workspace = torch.empty((wsb,), dtype=torch.uint8, device=x.device)
+    workspace = _workspace(workspace, wsb, x.device)
     fn = "fp8_act_quant_block_tensor"
     with torch.cuda.device(x.device):
         rc = getattr(lib(), fn)(_ptr(x), M, K, _ptr(qb), _ptr(sb), _ptr(qt), _ptr(st), _ptr(workspace),
-                                workspace.numel() if workspace is not None else 0,
-                                ctypes.c_void_p(_stream(x.device)))
+                                _nbytes(workspace), ctypes.c_void_p(_stream(x.device)))
     _check(fn, rc)
     return qb, sb, qt, st
 
@@ -274,14 +323,16 @@ def _gemm(fn, a, a_scale, w, w_scale, out, workspace, per_tensor=False):
             raise ValueError("a_scale and w_scale must hold one value each")
     elif a_scale.shape != (M, K // 128) or w_scale.shape != (N // 128, K // 128):
         raise ValueError("a_scale must be [M, K/128] and w_scale [N/128, K/128]")
-    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    if out is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    else:
+        c = _out(out, "out", _BF16, (M, N), a.device)
     wsb = fp8_gemm_blockscaled_workspace_bytes(M, N, K)
-    if workspace is None and wsb > 0:
-        workspace = torch.empty((wsb,), dtype=torch.uint8, device=a.device)
+    workspace = _workspace(workspace, wsb, a.device)
     with torch.cuda.device(a.device):
         rc = getattr(lib(), fn)(
             _ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(c), M, N, K, _ptr(workspace),
-            workspace.numel() if workspace is not None else 0, ctypes.c_void_p(_stream(a.device)))
+            _nbytes(workspace), ctypes.c_void_p(_stream(a.device)))
     _check(fn, rc)
     return c
 
@@ -323,15 +374,17 @@ def fp8_act_quant_gemm_blockscaled(x, w, w_scale, out=None, workspace=None):
     N = w.shape[0]
     if w_scale.shape != (N // 128, K // 128):
         raise ValueError("w_scale must be [N/128, K/128]")
-    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if out is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        c = _out(out, "out", _BF16, (M, N), x.device)
     wsb = fp8_act_quant_gemm_blockscaled_workspace_bytes(M, N, K)
-    if workspace is None and wsb > 0:
-        workspace = torch.empty((wsb,), dtype=torch.uint8, device=x.device)
+    workspace = _workspace(workspace, wsb, x.device)
     fn = "fp8_act_quant_gemm_blockscaled"
     with torch.cuda.device(x.device):
         rc = getattr(lib(), fn)(
             _ptr(x), _ptr(w), _ptr(w_scale), _ptr(c), M, N, K, _ptr(workspace),
-            workspace.numel() if workspace is not None else 0, ctypes.c_void_p(_stream(x.device)))
+            _nbytes(workspace), ctypes.c_void_p(_stream(x.device)))
     _check(fn, rc)
     return c
 
@@ -341,11 +394,14 @@ def _weight_quant(fn, w: torch.Tensor, out):
     if w.dim() != 2:
         raise ValueError("w must be 2-D [N, K]")
     N, K = w.shape
+    sshape = (max(N // 128, 1), max(K // 128, 1))
     if out is None:
         q = torch.empty((N, K), dtype=E4M3, device=w.device)
-        s = torch.empty((max(N // 128, 1), max(K // 128, 1)), dtype=torch.float32, device=w.device)
+        s = torch.empty(sshape, dtype=torch.float32, device=w.device)
     else:
         q, s = out
+        _out(q, "q", _CODES, (N, K), w.device)
+        _out(s, "scale", _F32, sshape, w.device)
     with torch.cuda.device(w.device):
         rc = getattr(lib(), fn)(_ptr(w), N, K, _ptr(q), _ptr(s), ctypes.c_void_p(_stream(w.device)))
     _check(fn, rc)
@@ -365,8 +421,27 @@ def fp8_weight_quant_block_ue8m0(w: torch.Tensor, out=None):
 def debug_encode_e4m3(v: torch.Tensor, out=None):
     """Test hook: the library's fp32 -> e4m3 rounding, elementwise."""
     _need(v, "v", torch.float32)
-    o = out if out is not None else torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    o = torch.empty(v.shape, dtype=torch.uint8, device=v.device) if out is None else \
+        _out(out, "out", (torch.uint8,), v.shape, v.device)
     with torch.cuda.device(v.device):
         rc = lib().fp8bs_debug_encode_e4m3(_ptr(v), _ptr(o), v.numel(), ctypes.c_void_p(_stream(v.device)))
     _check("fp8bs_debug_encode_e4m3", rc)
     return o
+
+
+def debug_mfma_block(a: torch.Tensor, w: torch.Tensor, out=None):
+    """Test hook: the matrix cores' fp32 dot products of one K block.
+    a, w: uint8 [tiles, 16, 128] codes; returns d float32 [tiles, 16, 16]
+    with d[t, n, m] = sum_k w[t, n, k] * a[t, m, k]."""
+    a, w = _as_u8(a), _as_u8(w)
+    _need(a, "a", torch.uint8)
+    _need(w, "w", torch.uint8, a.device)
+    if a.dim() != 3 or tuple(a.shape[1:]) != (16, 128) or a.shape != w.shape:
+        raise ValueError("a and w must both be [tiles, 16, 128]")
+    tiles = a.shape[0]
+    d = torch.empty((tiles, 16, 16), dtype=torch.float32, device=a.device) if out is None else \
+        _out(out, "out", _F32, (tiles, 16, 16), a.device)
+    with torch.cuda.device(a.device):
+        rc = lib().fp8bs_debug_mfma_block(_ptr(a), _ptr(w), _ptr(d), tiles, ctypes.c_void_p(_stream(a.device)))
+    _check("fp8bs_debug_mfma_block", rc)
+    return d

@@ -22,14 +22,6 @@
 #include "device_common.h"
 #include "host_common.h"
 
-// Build-time knobs kept for measurement (the defaults are the measured best):
-// FP8BS_DMA_ROWS, the MFMA rows of a block over which the next block's copies
-// are spread; FP8BS_DEC_WAVES, the waves of a small-M decode workgroup;
-// FP8BS_GEMM_TILE, 0 to pick the tile shape by problem size, else one shape
-// for every size (1: 128x128, 2: 256x256, 3: 256x128 with three stages).
-#ifndef FP8BS_DMA_ROWS
-#define FP8BS_DMA_ROWS 4
-#endif
 namespace fp8bs {
 namespace {
 
@@ -40,6 +32,10 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 128;     // K block
 constexpr int kGroupM = 8;   // m tiles walked per n tile (tile order)
+// MFMA rows of a block over which the copies of the block being prefetched
+// are spread (measured on the prefill shape: rows 0-3 109.1 us, all at once
+// 118.8 us, over all eight rows 115.5 us)
+constexpr int kDmaRows = 4;
 
 __device__ __forceinline__ v4f mfma_16x16x128_fp8(const v8i& a, const v8i& b) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -338,8 +334,8 @@ void gemm_blockscaled_tiled_kernel(
   }
   wlast = v8i{0, 0, 0, 0, 0, 0, 0, 0};
   // copies of the prefetched block: kPerRow per MFMA row, rows 0..kDmaRows-1
-  constexpr int kDmaRows = FP8BS_DMA_ROWS < NI - 1 ? FP8BS_DMA_ROWS : NI - 1;
-  constexpr int kPerRow = (kPer + kDmaRows - 1) / kDmaRows;
+  constexpr int kRows = kDmaRows < NI - 1 ? kDmaRows : NI - 1;
+  constexpr int kPerRow = (kPer + kRows - 1) / kRows;
   static_assert((kPer + kPerRow - 1) / kPerRow <= NI - 1, "every copy must be issued");
 
   // One K block. PF: the block STAGES-1 ahead is copied in during this one
@@ -570,10 +566,7 @@ void gemm_blockscaled_tiled_kernel(
 // (l%16)/R; its four outputs lie in one group, and they are kept when that
 // group is its own column's.
 // ---------------------------------------------------------------------------
-#ifndef FP8BS_DEC_WAVES
-#define FP8BS_DEC_WAVES 16
-#endif
-constexpr int kDecWaves = FP8BS_DEC_WAVES;
+constexpr int kDecWaves = 16;
 constexpr int kDecStreamMaxM = 16;
 // K blocks packed into one MFMA for a small-M decode GEMM (rows per
 // workgroup 16 / P must hold the M activation rows)
@@ -1164,9 +1157,30 @@ int launch_decode(const uint8_t* a, const float* sa, const uint8_t* w, const flo
   return FP8BS_OK;
 }
 
-#ifndef FP8BS_GEMM_TILE
-#define FP8BS_GEMM_TILE 0
-#endif
+// Test hook: the matrix cores' dot product of one K block, as every GEMM
+// kernel here computes it (mfma_16x16x128_fp8, accumulator input 0). Tile t
+// holds 16 W rows and 16 A rows of 128 codes; the wave's lanes load them in
+// the fragment layout of the GEMM kernels and store the fp32 16x16 result
+// D[t][n][m] = sum_k W[t][n][k] * A[t][m][k].
+__global__ __launch_bounds__(64) void debug_mfma_block_kernel(const uint8_t* __restrict__ A,
+                                                               const uint8_t* __restrict__ W,
+                                                               float* __restrict__ D, int64_t tiles) {
+  const int64_t t = blockIdx.x;
+  if (t >= tiles) return;
+  const int lane = threadIdx.x;
+  const int64_t off = t * 2048 + (lane & 15) * 128 + 32 * (lane >> 4);
+  const uint4 a0 = *reinterpret_cast<const uint4*>(A + off);
+  const uint4 a1 = *reinterpret_cast<const uint4*>(A + off + 16);
+  const uint4 w0 = *reinterpret_cast<const uint4*>(W + off);
+  const uint4 w1 = *reinterpret_cast<const uint4*>(W + off + 16);
+  const v8i af = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const v8i wf = v8i{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+  const v4f d = mfma_16x16x128_fp8(wf, af);
+  // lane holds D[n = 4 * (lane / 16) + r][m = lane % 16]
+  float* o = D + t * 256 + (lane & 15);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o[(4 * (lane >> 4) + r) * 16] = d[r];
+}
 
 template <int BN, int BM, int WN, int WM, int STAGES, int WPE, int MODE>
 int launch_tiled(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c,
@@ -1181,6 +1195,18 @@ int launch_tiled(const uint8_t* a, const float* sa, const uint8_t* w, const floa
   return FP8BS_OK;
 }
 
+// Sizes every GEMM entry point accepts: K and N multiples of 128, products
+// that fit int64, K at most 2^22, and for the split-K decode kernel at most
+// kDecMaxSplits * kDecMaxKb K blocks.
+inline bool gemm_shape_ok(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return false;
+  if (M > (INT64_MAX / K) || M > (INT64_MAX / N) || N > (INT64_MAX / K)) return false;
+  if (K > (int64_t{1} << 22) || (M + 127) / 128 > 0x7FFFFFFF) return false;
+  if (use_decode(M) && M > kDecStreamMaxM && K / 128 > static_cast<int64_t>(kDecMaxSplits) * kDecMaxKb)
+    return false;
+  return true;
+}
+
 }  // namespace
 }  // namespace fp8bs
 
@@ -1189,7 +1215,7 @@ using namespace fp8bs;
 extern "C" {
 
 size_t fp8_gemm_blockscaled_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return 0;
+  if (!gemm_shape_ok(M, N, K)) return 0;
   return use_decode(M) && M > kDecStreamMaxM ? decode_workspace_bytes(M, N, K) : 0;
 }
 
@@ -1202,11 +1228,7 @@ int gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m
                      void* c_bf16, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
                      void* stream) {
   if (!a_e4m3 || !a_scale || !w_e4m3 || !w_scale || !c_bf16) return FP8BS_ERR_NULL;
-  if (M < 1 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return FP8BS_ERR_SHAPE;
-  if (M > (INT64_MAX / K) || M > (INT64_MAX / N) || N > (INT64_MAX / K)) return FP8BS_ERR_SHAPE;
-  if (K > (int64_t{1} << 22) || (M + 127) / 128 > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
-  if (use_decode(M) && M > kDecStreamMaxM && K / 128 > static_cast<int64_t>(kDecMaxSplits) * kDecMaxKb)
-    return FP8BS_ERR_SHAPE;
+  if (!gemm_shape_ok(M, N, K)) return FP8BS_ERR_SHAPE;
   if (!aligned(a_e4m3, 16) || !aligned(w_e4m3, 16) || !aligned(c_bf16, 16) ||
       !aligned(a_scale, 4) || !aligned(w_scale, 4))
     return FP8BS_ERR_ALIGN;
@@ -1230,7 +1252,6 @@ int gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m
     if (rc != FP8BS_OK) return rc;
     return launch_status();
   }
-#if FP8BS_GEMM_TILE == 0
   // 256 x 256 tiles (eight waves, two per SIMD) when they fill the chip,
   // else 128 x 128 tiles (two workgroups per CU)
   const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
@@ -1238,13 +1259,6 @@ int gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m
     rc = launch_tiled<256, 256, 2, 4, 2, 2, MODE>(a, a_scale, w, w_scale, c, M, N, K, st);
   else
     rc = launch_tiled<128, 128, 2, 2, 2, 2, MODE>(a, a_scale, w, w_scale, c, M, N, K, st);
-#elif FP8BS_GEMM_TILE == 1
-  rc = launch_tiled<128, 128, 2, 2, 2, 2, MODE>(a, a_scale, w, w_scale, c, M, N, K, st);
-#elif FP8BS_GEMM_TILE == 2
-  rc = launch_tiled<256, 256, 2, 4, 2, 2, MODE>(a, a_scale, w, w_scale, c, M, N, K, st);
-#elif FP8BS_GEMM_TILE == 3
-  rc = launch_tiled<256, 128, 2, 2, 3, 1, MODE>(a, a_scale, w, w_scale, c, M, N, K, st);
-#endif
   if (rc != FP8BS_OK) return rc;
   return launch_status();
 }
@@ -1280,10 +1294,10 @@ int fp8_gemm_tensorscaled(const void* a_e4m3, const float* a_scale, const void* 
 namespace fp8bs {
 namespace {
 inline int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+// the two-launch form runs the GEMM's own checks, so the call accepts what
+// the GEMM accepts (the one-kernel form has no further limit)
 inline bool act_gemm_shape_ok(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return false;
-  if (M > (INT64_MAX / K) || M > (INT64_MAX / N) || N > (INT64_MAX / K)) return false;
-  return K <= (int64_t{1} << 22);
+  return gemm_shape_ok(M, N, K);
 }
 }  // namespace
 }  // namespace fp8bs
@@ -1322,6 +1336,22 @@ int fp8_act_quant_gemm_blockscaled(const void* x_bf16, const void* w_e4m3, const
   if (rc != FP8BS_OK) return rc;
   return fp8_gemm_blockscaled(q, sa, w_e4m3, w_scale, c_bf16, M, N, K, gws_bytes ? gws : nullptr, gws_bytes,
                               stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int fp8bs_debug_mfma_block(const void* a_e4m3, const void* w_e4m3, float* d, int64_t tiles, void* stream) {
+  if (!a_e4m3 || !w_e4m3 || !d) return FP8BS_ERR_NULL;
+  if (tiles < 1 || tiles > 0x7FFFFFFF) return FP8BS_ERR_SHAPE;
+  if (!aligned(a_e4m3, 16) || !aligned(w_e4m3, 16) || !aligned(d, 4)) return FP8BS_ERR_ALIGN;
+  const DeviceInfo dev = current_device();
+  if (dev.status != FP8BS_OK) return dev.status;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(debug_mfma_block_kernel, dim3(static_cast<unsigned>(tiles)), dim3(64), 0, as_stream(stream),
+                     static_cast<const uint8_t*>(a_e4m3), static_cast<const uint8_t*>(w_e4m3), d, tiles);
+  return launch_status();
 }
 
 }  // extern "C"

@@ -447,6 +447,7 @@ const char* fp8bs_status_string(int status) {
     case FP8BS_ERR_WORKSPACE: return "FP8BS_ERR_WORKSPACE: workspace missing or too small";
     case FP8BS_ERR_DEVICE: return "FP8BS_ERR_DEVICE: no HIP device or device is not gfx950";
     case FP8BS_ERR_LAUNCH: return "FP8BS_ERR_LAUNCH: kernel launch failed";
+    case FP8BS_ERR_INTERNAL: return "FP8BS_ERR_INTERNAL: a HIP runtime query needed for set-up failed";
     default: return "FP8BS_ERR_UNKNOWN";
   }
 }

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code in range(7):
+    for code in range(8):
         s = L.fp8bs_status_string(code).decode()
         assert s.startswith("FP8BS_")
     assert L.fp8bs_status_string(99).decode() == "FP8BS_ERR_UNKNOWN"
@@ -95,6 +95,16 @@ def test_weight_quant_argument_errors(L):
     assert f(PU, 128, 128, P, P, None) == EALIGN
 
 
+def test_debug_mfma_block_argument_errors(L):
+    f = L.fp8bs_debug_mfma_block
+    assert f(None, P, P, 1, None) == ENULL
+    assert f(P, P, None, 1, None) == ENULL
+    assert f(P, P, P, 0, None) == ESHAPE
+    assert f(P, P, P, 1 << 31, None) == ESHAPE
+    assert f(PU, P, P, 1, None) == EALIGN
+    assert f(P, P, P + 2, 1, None) == EALIGN
+
+
 def test_debug_encode_argument_errors(L):
     f = L.fp8bs_debug_encode_e4m3
     assert f(None, P, 4, None) == ENULL
@@ -124,6 +134,11 @@ def test_gemm_k_limits(L):
     assert L.fp8_gemm_blockscaled(P, P, P, P, P, 32, 128, 128 * 513, None, 0, None) == ESHAPE
     assert L.fp8_gemm_blockscaled_workspace_bytes(8, 2048, 7168) == 0
     assert L.fp8_gemm_blockscaled_workspace_bytes(32, 2048, 7168) > 0
+    # a shape the call rejects needs no workspace, and the act-quant + GEMM
+    # call rejects it before enqueuing anything
+    assert L.fp8_gemm_blockscaled_workspace_bytes(32, 128, 128 * 513) == 0
+    assert L.fp8_act_quant_gemm_blockscaled_workspace_bytes(32, 128, 128 * 513) == 0
+    assert L.fp8_act_quant_gemm_blockscaled(P, P, P, P, 32, 128, 128 * 513, P, 1 << 30, None) == ESHAPE
 
 
 def test_ue8m0_argument_errors(L):
