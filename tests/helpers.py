@@ -47,3 +47,12 @@ def binding():
 def say(*args):
     """Name the case before a GPU step (flushed, so a crash still shows it)."""
     print("[case]", *args, flush=True)
+
+
+def report(label, res):
+    """Print a GEMM comparison: normwise error, worst elementwise ratio and
+    the share of outputs within plain 4 bf16 ulp + the fp32 floor first
+    proposed for the comparison (oracle.gemm.s13_tau)."""
+    print(f"[gemm] {label}: normwise {res['normwise']:.3e}, elementwise ratio {res['elem_ratio']:.3f}, "
+          f"within 4 ulp + fp32 floor {res['frac_plain']:.6f} ({res['n'] - res['n_plain']} of {res['n']} outside)",
+          flush=True)

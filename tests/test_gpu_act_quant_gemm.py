@@ -13,7 +13,7 @@ import torch
 
 import synth
 from oracle import gemm, quant
-from tests.helpers import bf16_to_dev, binding, say, to_bf16_bits
+from tests.helpers import bf16_to_dev, binding, report, say, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -42,11 +42,8 @@ def run_two_calls(x_bits, qw, sw):
 
 def check_oracle(c, x_bits, qw, sw, label):
     qa, sa = quant.act_quant_block(x_bits)
-    R = gemm.gemm_blockscaled_ref(qa, sa, qw, sw)
-    S = gemm.gemm_abs_ref(qa, sa, qw, sw)
-    Se = gemm.gemm_exp_envelope_ref(qa, sa, qw, sw)
-    res = gemm.compare_gemm(c, R, S, qa.shape[1], Se)
-    say("  ", label, {k: res[k] for k in res if k != "ok"})
+    res = gemm.compare_gemm_full(c, qa, sa, qw, sw)
+    report(label, res)
     assert res["ok"], (label, res)
 
 
