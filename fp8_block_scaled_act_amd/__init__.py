@@ -32,6 +32,7 @@ __all__ = [
     "fp8_act_quant_block",
     "fp8_amax_quant_tensor",
     "fp8_amax_quant_tensor_workspace_bytes",
+    "fp8_amax_quant_tensor_noalloc",
     "fp8_gemm_blockscaled",
     "fp8_gemm_blockscaled_workspace_bytes",
     "fp8_weight_quant_block",
@@ -57,6 +58,7 @@ EXPORTED_SYMBOLS = (
     "fp8_act_quant_block",
     "fp8_amax_quant_tensor_workspace_bytes",
     "fp8_amax_quant_tensor",
+    "fp8_amax_quant_tensor_noalloc",
     "fp8_gemm_blockscaled_workspace_bytes",
     "fp8_gemm_blockscaled",
     "fp8_weight_quant_block",
@@ -106,6 +108,8 @@ def lib() -> ctypes.CDLL:
     L.fp8_amax_quant_tensor_workspace_bytes.restype = sz
     L.fp8_amax_quant_tensor.argtypes = [vp, i64, vp, fp, vp, sz, vp]
     L.fp8_amax_quant_tensor.restype = ctypes.c_int
+    L.fp8_amax_quant_tensor_noalloc.argtypes = [vp, i64, vp, fp, vp]
+    L.fp8_amax_quant_tensor_noalloc.restype = ctypes.c_int
     L.fp8_gemm_blockscaled_workspace_bytes.argtypes = [i64, i64, i64]
     L.fp8_gemm_blockscaled_workspace_bytes.restype = sz
     L.fp8_gemm_blockscaled.argtypes = [vp, fp, vp, fp, vp, i64, i64, i64, vp, sz, vp]
@@ -260,6 +264,25 @@ def fp8_amax_quant_tensor(x: torch.Tensor, out=None, workspace=None):
             _ptr(x), numel, _ptr(q), _ptr(s), _ptr(workspace), _nbytes(workspace),
             ctypes.c_void_p(_stream(x.device)))
     _check("fp8_amax_quant_tensor", rc)
+    return q, s
+
+
+def fp8_amax_quant_tensor_noalloc(x: torch.Tensor, out=None):
+    """fp8_amax_quant_tensor with its scratch in the library's own device
+    array: the C call allocates nothing (pass ``out`` to allocate nothing
+    here either). Calls that overlap on one GPU race."""
+    _need(x, "x", torch.bfloat16)
+    if out is None:
+        q = torch.empty(x.shape, dtype=E4M3, device=x.device)
+        s = torch.empty((1,), dtype=torch.float32, device=x.device)
+    else:
+        q, s = out
+        _out(q, "q", _CODES, x.shape, x.device)
+        _out(s, "scale", _F32, (1,), x.device)
+    with torch.cuda.device(x.device):
+        rc = lib().fp8_amax_quant_tensor_noalloc(_ptr(x), x.numel(), _ptr(q), _ptr(s),
+                                                 ctypes.c_void_p(_stream(x.device)))
+    _check("fp8_amax_quant_tensor_noalloc", rc)
     return q, s
 
 

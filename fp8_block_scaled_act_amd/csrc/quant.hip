@@ -536,18 +536,15 @@ size_t fp8_amax_quant_tensor_workspace_bytes(int64_t numel) {
   return numel > kSmallNumel ? kMaxPartials * sizeof(float) : 0;
 }
 
-int fp8_amax_quant_tensor(const void* x_bf16, int64_t numel, void* q_e4m3, float* scale,
-                          void* workspace, size_t workspace_bytes, void* stream) {
-  if (!x_bf16 || !q_e4m3 || !scale) return FP8BS_ERR_NULL;
-  if (numel < 1) return FP8BS_ERR_SHAPE;
-  if (!aligned(x_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(scale, 4)) return FP8BS_ERR_ALIGN;
-  const size_t need = fp8_amax_quant_tensor_workspace_bytes(numel);
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need) return FP8BS_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return FP8BS_ERR_ALIGN;
-  }
-  const DeviceInfo dev = current_device();
-  if (dev.status != FP8BS_OK) return dev.status;
+}  // extern "C"
+
+namespace fp8bs {
+namespace {
+// The two launches of the per-tensor quantization (one for small inputs);
+// `partial` holds at least fp8_amax_quant_tensor_workspace_bytes(numel)
+// bytes. Arguments are checked by the callers.
+int amax_quant_tensor_launch(const void* x_bf16, int64_t numel, void* q_e4m3, float* scale, float* partial,
+                             const DeviceInfo& dev, void* stream) {
   hipStream_t st = as_stream(stream);
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
   uint8_t* q = static_cast<uint8_t*>(q_e4m3);
@@ -557,7 +554,6 @@ int fp8_amax_quant_tensor(const void* x_bf16, int64_t numel, void* q_e4m3, float
                        numel);
     return launch_status();
   }
-  float* partial = static_cast<float*>(workspace);
   const int g = tensor_grid(numel, dev.num_cus);
   hipLaunchKernelGGL(tensor_amax_partial_kernel, dim3(g), dim3(kThreads), 0, st, x, partial,
                      numel);
@@ -568,6 +564,76 @@ int fp8_amax_quant_tensor(const void* x_bf16, int64_t numel, void* q_e4m3, float
   hipLaunchKernelGGL(tensor_apply_kernel, dim3(static_cast<unsigned>(ga)), dim3(kThreads), 0, st, x,
                      q, scale, partial, g, numel);
   return launch_status();
+}
+
+int amax_quant_tensor_check(const void* x_bf16, int64_t numel, void* q_e4m3, float* scale) {
+  if (!x_bf16 || !q_e4m3 || !scale) return FP8BS_ERR_NULL;
+  if (numel < 1) return FP8BS_ERR_SHAPE;
+  if (!aligned(x_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(scale, 4)) return FP8BS_ERR_ALIGN;
+  return FP8BS_OK;
+}
+
+// Scratch of the allocation-free per-tensor quantization: the partial maxima
+// of its first pass, in a device array of the library's own (zero-filled
+// when the code object loads, and only ever written before it is read, so
+// nothing needs clearing). Host code never uses the array's name, which on
+// the host is a stand-in and not a device address: it uses the address that
+// hipGetSymbolAddress returns for the current device, looked up on the first
+// call on each device and kept per device.
+constexpr size_t kScratchBytes = kMaxPartials * sizeof(float);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+void* scratch_address(int* status) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<void*> addr[kMaxDev];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    (void)hipGetLastError();
+    *status = FP8BS_ERR_DEVICE;
+    return nullptr;
+  }
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      *status = FP8BS_ERR_INTERNAL;
+      return nullptr;
+    }
+    addr[dev].store(p, std::memory_order_release);   // the same value from every thread
+  }
+  *status = FP8BS_OK;
+  return p;
+}
+}  // namespace
+}  // namespace fp8bs
+
+extern "C" {
+
+int fp8_amax_quant_tensor(const void* x_bf16, int64_t numel, void* q_e4m3, float* scale,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = amax_quant_tensor_check(x_bf16, numel, q_e4m3, scale);
+  if (rc != FP8BS_OK) return rc;
+  const size_t need = fp8_amax_quant_tensor_workspace_bytes(numel);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return FP8BS_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return FP8BS_ERR_ALIGN;
+  }
+  const DeviceInfo dev = current_device();
+  if (dev.status != FP8BS_OK) return dev.status;
+  return amax_quant_tensor_launch(x_bf16, numel, q_e4m3, scale, static_cast<float*>(workspace), dev, stream);
+}
+
+int fp8_amax_quant_tensor_noalloc(const void* x_bf16, int64_t numel, void* q_e4m3, float* scale, void* stream) {
+  const int rc = amax_quant_tensor_check(x_bf16, numel, q_e4m3, scale);
+  if (rc != FP8BS_OK) return rc;
+  // the first pass writes at most kMaxPartials partial maxima, whatever numel
+  if (fp8_amax_quant_tensor_workspace_bytes(numel) > kScratchBytes) return FP8BS_ERR_WORKSPACE;
+  const DeviceInfo dev = current_device();
+  if (dev.status != FP8BS_OK) return dev.status;
+  int st = FP8BS_OK;
+  void* partial = scratch_address(&st);
+  if (st != FP8BS_OK) return st;
+  return amax_quant_tensor_launch(x_bf16, numel, q_e4m3, scale, static_cast<float*>(partial), dev, stream);
 }
 
 size_t fp8_act_quant_block_tensor_workspace_bytes(int64_t M, int64_t K) {

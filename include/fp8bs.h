@@ -105,6 +105,21 @@ int fp8_amax_quant_tensor(const void* x_bf16, int64_t numel,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fp8_amax_quant_tensor without a workspace argument, for callers that
+ * cannot allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid allocation. The same kernels and
+ * results, bit for bit; the partial maxima of the first pass (at most 1024
+ * floats, 4 KiB, for every numel) go to a device array of the library's own,
+ * one per GPU, which holds 4 KiB of device memory until the process ends.
+ * The call allocates nothing. Calls that overlap on one GPU (concurrent
+ * streams, host threads) share that array and race: serialize them.
+ * Arguments, layouts and errors as fp8_amax_quant_tensor; FP8BS_ERR_INTERNAL
+ * if the array's device address cannot be obtained.
+ */
+int fp8_amax_quant_tensor_noalloc(const void* x_bf16, int64_t numel,
+                                  void* q_e4m3, float* scale, void* stream);
+
+/*
  * Block-scaled FP8 GEMM with bf16 output: C = A . W^T.
  * DeepSeek-V3 fp8_gemm_kernel ("How to Profile DeepSeek-V3 Inference Kernels
  * Using Triton Autotuning", sections "Understanding the Autotuned Kernels in

@@ -72,6 +72,15 @@ def test_tensor_quant_argument_errors(L):
     assert f(P, big, P, P, PU, ws(big), None) == EALIGN
 
 
+def test_tensor_quant_noalloc_argument_errors(L):
+    f = L.fp8_amax_quant_tensor_noalloc
+    assert f(None, 10, P, P, None) == ENULL
+    assert f(P, 10, None, P, None) == ENULL
+    assert f(P, 0, P, P, None) == ESHAPE
+    assert f(PU, 10, P, P, None) == EALIGN
+    assert f(P, 10, P, P + 2, None) == EALIGN
+
+
 def test_gemm_argument_errors(L):
     f = L.fp8_gemm_blockscaled
     assert f(None, P, P, P, P, 4, 128, 128, None, 0, None) == ENULL
@@ -116,6 +125,7 @@ def test_debug_encode_argument_errors(L):
 def test_valid_arguments_without_a_device_report_device_error(L):
     # all arguments valid: the next step is the device check, which fails here
     assert L.fp8_act_quant_block(P, 4, 128, P, P, None) == EDEV
+    assert L.fp8_amax_quant_tensor_noalloc(P, 1 << 20, P, P, None) == EDEV
     assert L.fp8_gemm_blockscaled(P, P, P, P, P, 4, 128, 128, None, 0, None) == EDEV
 
 
