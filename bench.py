@@ -13,6 +13,10 @@ N=2048, K=7168), c2 per-tensor sweep (K=2048), c1 tiny (32x512x512).
 
 Prints ONE JSON line. ``value`` is the step throughput expressed as GEMM
 TFLOP/s (2*M*N*K per step / step time; per-tensor-only workloads use GB/s).
+The default run also times every other workload the same way and reports
+them under ``configs`` (c1; c2 per M with the amax stage alone beside the
+TensorRT-LLM page's B200 figures; c3 per M as two calls and as the fused
+call; c4); --no-sweep leaves that out.
 The per-stage times come from HIP events around back-to-back launches of
 each stage alone on the launch stream (replayed from a graph of their own
 under --graph); ``roofline`` is for the dominant kernel. ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
@@ -62,6 +66,8 @@ def parse():
     p.add_argument("--separate-quant", action="store_true",
                    help="large-M workload: block and per-tensor quant as two calls (default: one call)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-sweep", dest="sweep", action="store_false", default=True,
+                   help="default large-M run only: leave out the other workloads' figures (key 'configs')")
     p.add_argument("--cpu-rows", type=int, default=None, help="rows of the CPU oracle sample")
     return p.parse_args()
 
@@ -95,7 +101,8 @@ class Workload:
         dev = "cuda:0"
         w = args.workload
         self.name = w
-        self.stages = []          # (name, fn(i) -> None, algorithmic bytes, flops)
+        self.stages = []          # (name, fn(i) -> None, algorithmic bytes, flops): one step
+        self.extra = []           # stages timed on their own only (not part of a step)
 
         def rotation(per_copy_bytes):
             # cache honesty: the copies a stage cycles through span at least
@@ -134,6 +141,11 @@ class Workload:
             self.stages.append(("amax_quant_tensor",
                                 lambda i: fb.fp8_amax_quant_tensor(xs[i % rot], out=(q, s), workspace=ws),
                                 3 * numel + 4, 0))
+            amax = torch.empty((1,), dtype=torch.float32, device=dev)
+            sa_only = torch.empty((1,), dtype=torch.float32, device=dev)
+            self.extra.append(("amax_tensor",
+                               lambda i: fb.fp8_amax_tensor(xs[i % rot], out=(amax, sa_only), workspace=ws),
+                               2 * numel + 8, 0))
             self.config = {"workload": f"per-tensor dynamic quant, X bf16 [{M}, {K}]", "M": M, "K": K}
             self.M, self.N, self.K = M, 0, K
             self.cpu = ("c2", M, K, None)
@@ -307,7 +319,7 @@ def time_steps(torch, wl, steps, warmup, graph):
     step_ms = e0.elapsed_time(e1) / steps
 
     per_stage = []
-    for _, fn, _, _ in wl.stages:
+    for _, fn, _, _ in wl.stages + wl.extra:
         gs = None
         if graph:
             # the stage's launches alone, replayed from a graph of their own
@@ -400,6 +412,84 @@ def cpu_baseline(wl, rows_arg, ue8m0=False):
                        f"{t:.2f} s; value = 2*rows*N*K / time")}
 
 
+def summarize(wl, per_stage, scale_fmt="fp32", workload_key=None):
+    """Per-stage figures (us per launch, spread, GB/s and TFLOP/s with their
+    roofline fractions) and the roofline object of the dominant kernel."""
+    stages = {}
+    for j, (name, _, nbytes, flops) in enumerate(wl.stages + wl.extra):
+        e = {"algorithmic_bytes": nbytes}
+        avg_ms, (med, p10, p90) = per_stage[j]
+        us = float(avg_ms) * 1e3
+        e["us_per_launch"] = us
+        e["us_median"], e["us_p10"], e["us_p90"] = med * 1e3, p10 * 1e3, p90 * 1e3
+        e["GB/s"] = nbytes / (us * 1e-6) / 1e9
+        e["hbm_frac"] = e["GB/s"] / HBM_PEAK_GBS
+        if flops:
+            e["TFLOP/s"] = flops / (us * 1e-6) / 1e12
+            e["mfma_frac"] = e["TFLOP/s"] / FP8_PEAK_TFLOPS
+        stages[name] = e
+    # dominant kernel: the GEMM when present (prefill: MFMA-bound; decode: HBM-bound)
+    if "gemm_blockscaled" in stages:
+        dominant = "gemm_blockscaled"
+    elif "act_quant_gemm_blockscaled" in stages:
+        dominant = "act_quant_gemm_blockscaled"
+    else:
+        dominant = wl.stages[0][0]
+    ds = stages[dominant]
+    src = "gemm.hip" if "gemm" in dominant else "quant.hip"
+    fmt = "_ue8m0" if scale_fmt == "ue8m0" and dominant != "amax_quant_tensor" else ""
+    traffic = load_traffic(f"{dominant}{fmt}:{workload_key or wl.name}", src)
+    if "gemm" in dominant and 2 * wl.M * wl.N * wl.K / max(ds["algorithmic_bytes"], 1) > 625:
+        roofline = {"bound": "mfma", "achieved": ds["TFLOP/s"], "peak": FP8_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": ds["TFLOP/s"] / FP8_PEAK_TFLOPS, "traffic": traffic}
+    else:
+        roofline = {"bound": "hbm", "achieved": ds["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": ds["GB/s"] / HBM_PEAK_GBS, "traffic": traffic}
+    roofline["kernel"] = dominant
+    roofline["us_per_launch"] = ds["us_per_launch"]
+    return stages, roofline
+
+
+# the TensorRT-LLM page's B200 amax-stage times (section "Test Coverage", the
+# fixed design, under CUDA graph), per M at K = 2048: context, not a target
+B200_AMAX_US = {1: 4.1, 64: 4.1, 256: 6.1, 1024: 6.1, 65536: 43.0}
+
+
+def sweep(torch, fb, steps, warmup, graph):
+    """Every other workload, timed the same way (inputs resident, rotated,
+    stages replayed from graphs): us per call, GB/s or TFLOP/s and the
+    roofline fraction of each stage, and the step time."""
+    from types import SimpleNamespace
+
+    def one(workload, M=None, fused=False):
+        spec = SimpleNamespace(workload=workload, M=M, rotate=0, scale_fmt="fp32", fused=fused,
+                               separate_quant=False)
+        wl = Workload(spec, torch, fb)
+        ms, per_stage, _ = time_steps(torch, wl, steps, warmup, graph)
+        stages, roofline = summarize(wl, per_stage, workload_key=workload)
+        keep = ("us_per_launch", "us_median", "GB/s", "hbm_frac", "TFLOP/s", "mfma_frac")
+        out = {"step_us": ms * 1e3,
+               "stages": {k: {f: round(v[f], 4) for f in keep if f in v} for k, v in stages.items()},
+               "roofline": {k: roofline[k] for k in ("kernel", "bound", "achieved", "unit", "frac")},
+               "rotated_copies": wl.rot}
+        del wl
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        return out
+
+    res = {"c1": one("c1")}
+    c2 = {}
+    for M in (1, 64, 256, 1024, 65536):
+        r = one("c2", M)
+        r["b200_amax_us_context"] = B200_AMAX_US[M]
+        c2[f"M={M}"] = r
+    res["c2"] = c2
+    res["c3"] = {f"M={M}": {"two_calls": one("c3", M), "fused_call": one("c3", M, fused=True)}
+                 for M in (1, 8, 32, 64)}
+    res["c4"] = one("c4")
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -415,43 +505,8 @@ def main():
     torch.cuda.set_device(0)
     wl = Workload(args, torch, fb)
     ms, per_stage, wall = time_steps(torch, wl, args.steps, args.warmup, args.graph)
-
-    stages = {}
-    dominant = None
-    for j, (name, _, nbytes, flops) in enumerate(wl.stages):
-        e = {"algorithmic_bytes": nbytes}
-        if per_stage is not None:
-            avg_ms, (med, p10, p90) = per_stage[j]
-            us = float(avg_ms) * 1e3
-            e["us_per_launch"] = us
-            e["us_median"], e["us_p10"], e["us_p90"] = med * 1e3, p10 * 1e3, p90 * 1e3
-            e["GB/s"] = nbytes / (us * 1e-6) / 1e9
-            e["hbm_frac"] = e["GB/s"] / HBM_PEAK_GBS
-            if flops:
-                e["TFLOP/s"] = flops / (us * 1e-6) / 1e12
-                e["mfma_frac"] = e["TFLOP/s"] / FP8_PEAK_TFLOPS
-        stages[name] = e
-    # dominant kernel: the GEMM when present (prefill: MFMA-bound; decode: HBM-bound)
-    if "gemm_blockscaled" in stages:
-        dominant = "gemm_blockscaled"
-    elif "act_quant_gemm_blockscaled" in stages:
-        dominant = "act_quant_gemm_blockscaled"
-    else:
-        dominant = wl.stages[0][0]
-    roofline = None
-    ds = stages[dominant]
-    if per_stage is not None:
-        src = "gemm.hip" if "gemm" in dominant else "quant.hip"
-        fmt = "_ue8m0" if args.scale_fmt == "ue8m0" and dominant != "amax_quant_tensor" else ""
-        traffic = load_traffic(f"{dominant}{fmt}:{args.workload}", src)
-        if "gemm" in dominant and 2 * wl.M * wl.N * wl.K / max(ds["algorithmic_bytes"], 1) > 625:
-            roofline = {"bound": "mfma", "achieved": ds["TFLOP/s"], "peak": FP8_PEAK_TFLOPS,
-                        "unit": "TFLOP/s", "frac": ds["TFLOP/s"] / FP8_PEAK_TFLOPS, "traffic": traffic}
-        else:
-            roofline = {"bound": "hbm", "achieved": ds["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": ds["GB/s"] / HBM_PEAK_GBS, "traffic": traffic}
-        roofline["kernel"] = dominant
-        roofline["us_per_launch"] = ds["us_per_launch"]
+    stages, roofline = summarize(wl, per_stage, args.scale_fmt, args.workload)
+    wl_config, wl_rot = wl.config, getattr(wl, "rot", 1)
 
     if wl.N:
         value = 2.0 * wl.M * wl.N * wl.K / (ms * 1e-3) / 1e12
@@ -469,6 +524,13 @@ def main():
         except AttributeError:  # pragma: no cover
             pass
 
+    configs = None
+    if args.sweep and args.workload == "c5" and args.scale_fmt == "fp32" and not args.separate_quant:
+        del wl
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        configs = sweep(torch, fb, min(args.steps, 50), min(args.warmup, 10), args.graph)
+
     line = {
         "metric": "FP8 block-scaled GEMM TFLOP/s + act-quant GB/s (%roofline), 1 MI355X",
         "value": value,
@@ -482,9 +544,9 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8_e4m3 (fp32 accumulate, bf16 in/out)",
         "data": "synthetic (seeded numpy generators; inputs resident in HBM, "
-                f"{getattr(wl, 'rot', 1)} rotated input copies"
-                + (", >= 512 MiB of distinct inputs)" if args.rotate == 0 and getattr(wl, 'rot', 1) < 64 else ")"),
-        "config": wl.config,
+                f"{wl_rot} rotated input copies"
+                + (", >= 512 MiB of distinct inputs)" if args.rotate == 0 else ")"),
+        "config": None,
         "timing": ("step: HIP events around all steps" + (" (HIP graph replay)" if args.graph else "")
                    + "; stages: HIP events around back-to-back launches of each stage"
                    + (" (each stage replayed from a graph of its own)" if args.graph else "")
@@ -495,6 +557,9 @@ def main():
         "cpu_baseline": cpu,
         "wall_s_timed_region": wall,
     }
+    line["config"] = wl_config
+    if configs is not None:
+        line["configs"] = configs
     print(json.dumps(line), flush=True)
 
 

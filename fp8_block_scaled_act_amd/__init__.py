@@ -33,6 +33,7 @@ __all__ = [
     "fp8_amax_quant_tensor",
     "fp8_amax_quant_tensor_workspace_bytes",
     "fp8_amax_quant_tensor_noalloc",
+    "fp8_amax_tensor",
     "fp8_gemm_blockscaled",
     "fp8_gemm_blockscaled_workspace_bytes",
     "fp8_weight_quant_block",
@@ -59,6 +60,7 @@ EXPORTED_SYMBOLS = (
     "fp8_amax_quant_tensor_workspace_bytes",
     "fp8_amax_quant_tensor",
     "fp8_amax_quant_tensor_noalloc",
+    "fp8_amax_tensor",
     "fp8_gemm_blockscaled_workspace_bytes",
     "fp8_gemm_blockscaled",
     "fp8_weight_quant_block",
@@ -110,6 +112,8 @@ def lib() -> ctypes.CDLL:
     L.fp8_amax_quant_tensor.restype = ctypes.c_int
     L.fp8_amax_quant_tensor_noalloc.argtypes = [vp, i64, vp, fp, vp]
     L.fp8_amax_quant_tensor_noalloc.restype = ctypes.c_int
+    L.fp8_amax_tensor.argtypes = [vp, i64, fp, fp, vp, sz, vp]
+    L.fp8_amax_tensor.restype = ctypes.c_int
     L.fp8_gemm_blockscaled_workspace_bytes.argtypes = [i64, i64, i64]
     L.fp8_gemm_blockscaled_workspace_bytes.restype = sz
     L.fp8_gemm_blockscaled.argtypes = [vp, fp, vp, fp, vp, i64, i64, i64, vp, sz, vp]
@@ -265,6 +269,26 @@ def fp8_amax_quant_tensor(x: torch.Tensor, out=None, workspace=None):
             ctypes.c_void_p(_stream(x.device)))
     _check("fp8_amax_quant_tensor", rc)
     return q, s
+
+
+def fp8_amax_tensor(x: torch.Tensor, out=None, workspace=None):
+    """The amax stage alone: (amax, scale), one fp32 each, of bf16 ``x``."""
+    _need(x, "x", torch.bfloat16)
+    if out is None:
+        amax = torch.empty((1,), dtype=torch.float32, device=x.device)
+        s = torch.empty((1,), dtype=torch.float32, device=x.device)
+    else:
+        amax, s = out
+        _out(amax, "amax", _F32, (1,), x.device)
+        _out(s, "scale", _F32, (1,), x.device)
+    numel = x.numel()
+    wsb = fp8_amax_quant_tensor_workspace_bytes(numel) if numel > 0 else 0
+    workspace = _workspace(workspace, wsb, x.device)
+    with torch.cuda.device(x.device):
+        rc = lib().fp8_amax_tensor(_ptr(x), numel, _ptr(amax), _ptr(s), _ptr(workspace), _nbytes(workspace),
+                                   ctypes.c_void_p(_stream(x.device)))
+    _check("fp8_amax_tensor", rc)
+    return amax, s
 
 
 def fp8_amax_quant_tensor_noalloc(x: torch.Tensor, out=None):

@@ -371,6 +371,43 @@ __global__ __launch_bounds__(kThreads) void tensor_apply_kernel(
   if (head) scale[0] = s;
 }
 
+// The amax stage alone (fp8_amax_tensor): the exact amax and the scale.
+// Large inputs: tensor_amax_partial_kernel, then one workgroup reduces the
+// partial maxima; small inputs: one 1024-thread workgroup reads everything.
+__global__ __launch_bounds__(kThreads) void tensor_amax_final_kernel(const float* __restrict__ partial,
+                                                                     int npartial, float* __restrict__ amax_out,
+                                                                     float* __restrict__ scale) {
+  __shared__ float lds[kThreads / 64];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < npartial; i += kThreads) m = fmaxf(m, partial[i]);
+  const float amax = block_max<kThreads>(m, lds);
+  if (threadIdx.x == 0) {
+    amax_out[0] = amax;
+    scale[0] = div_ieee(amax, kE4m3Max);
+  }
+}
+
+__global__ __launch_bounds__(kSmallThreads) void tensor_amax_small_kernel(const uint16_t* __restrict__ x,
+                                                                          int64_t numel, float* __restrict__ amax_out,
+                                                                          float* __restrict__ scale) {
+  __shared__ float lds[kSmallThreads / 64];
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const int64_t nvec = numel >> 3;
+  const int64_t i0 = threadIdx.x, i1 = threadIdx.x + kSmallThreads;
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  const uint4 v0 = i0 < nvec ? xv[i0] : z;
+  const uint4 v1 = i1 < nvec ? xv[i1] : z;
+  float m = 0.0f;
+  m = absmax2(v0.x, m); m = absmax2(v0.y, m); m = absmax2(v0.z, m); m = absmax2(v0.w, m);
+  m = absmax2(v1.x, m); m = absmax2(v1.y, m); m = absmax2(v1.z, m); m = absmax2(v1.w, m);
+  if (threadIdx.x == 0) m = tail_absmax(x, nvec << 3, numel, m);
+  const float amax = block_max<kSmallThreads>(m, lds);
+  if (threadIdx.x == 0) {
+    amax_out[0] = amax;
+    scale[0] = div_ieee(amax, kE4m3Max);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Block and per-tensor quantization of the same X (both quantize the
 // activation of the large-M workload): the block kernel above, with
@@ -621,6 +658,33 @@ int fp8_amax_quant_tensor(const void* x_bf16, int64_t numel, void* q_e4m3, float
   const DeviceInfo dev = current_device();
   if (dev.status != FP8BS_OK) return dev.status;
   return amax_quant_tensor_launch(x_bf16, numel, q_e4m3, scale, static_cast<float*>(workspace), dev, stream);
+}
+
+int fp8_amax_tensor(const void* x_bf16, int64_t numel, float* amax, float* scale, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!x_bf16 || !amax || !scale) return FP8BS_ERR_NULL;
+  if (numel < 1) return FP8BS_ERR_SHAPE;
+  if (!aligned(x_bf16, 16) || !aligned(amax, 4) || !aligned(scale, 4)) return FP8BS_ERR_ALIGN;
+  const size_t need = fp8_amax_quant_tensor_workspace_bytes(numel);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return FP8BS_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return FP8BS_ERR_ALIGN;
+  }
+  const DeviceInfo dev = current_device();
+  if (dev.status != FP8BS_OK) return dev.status;
+  hipStream_t st = as_stream(stream);
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  (void)hipGetLastError();
+  if (numel <= kSmallNumel) {
+    hipLaunchKernelGGL(tensor_amax_small_kernel, dim3(1), dim3(kSmallThreads), 0, st, x, numel, amax, scale);
+    return launch_status();
+  }
+  float* partial = static_cast<float*>(workspace);
+  const int g = tensor_grid(numel, dev.num_cus);
+  hipLaunchKernelGGL(tensor_amax_partial_kernel, dim3(g), dim3(kThreads), 0, st, x, partial, numel);
+  if (hipGetLastError() != hipSuccess) return FP8BS_ERR_LAUNCH;
+  hipLaunchKernelGGL(tensor_amax_final_kernel, dim3(1), dim3(kThreads), 0, st, partial, g, amax, scale);
+  return launch_status();
 }
 
 int fp8_amax_quant_tensor_noalloc(const void* x_bf16, int64_t numel, void* q_e4m3, float* scale, void* stream) {

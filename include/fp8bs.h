@@ -105,6 +105,18 @@ int fp8_amax_quant_tensor(const void* x_bf16, int64_t numel,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The amax stage of the per-tensor quantization alone (TensorRT-LLM PR "Size
+ * the per-tensor FP8 dynamic-quant amax grid to the input", sections
+ * "Description" and "Test Coverage": the amax reduction is timed on its own):
+ *     amax[0] = max |x| (exact), scale[0] = fl32(amax / 448)
+ * with the grid and the partial maxima of fp8_amax_quant_tensor, whose
+ * workspace size applies (fp8_amax_quant_tensor_workspace_bytes). amax and
+ * scale are one fp32 each on the device. Errors as fp8_amax_quant_tensor.
+ */
+int fp8_amax_tensor(const void* x_bf16, int64_t numel, float* amax, float* scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fp8_amax_quant_tensor without a workspace argument, for callers that
  * cannot allocate device memory: code being captured into a HIP graph, tight
  * serving loops, harnesses that forbid allocation. The same kernels and

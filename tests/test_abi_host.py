@@ -72,6 +72,19 @@ def test_tensor_quant_argument_errors(L):
     assert f(P, big, P, P, PU, ws(big), None) == EALIGN
 
 
+def test_amax_only_argument_errors(L):
+    f = L.fp8_amax_tensor
+    big = 1 << 20
+    ws = L.fp8_amax_quant_tensor_workspace_bytes(big)
+    assert f(None, 10, P, P, None, 0, None) == ENULL
+    assert f(P, 10, None, P, None, 0, None) == ENULL
+    assert f(P, 0, P, P, None, 0, None) == ESHAPE
+    assert f(PU, 10, P, P, None, 0, None) == EALIGN
+    assert f(P, big, P, P, None, 0, None) == EWS
+    assert f(P, big, P, P, P, ws - 1, None) == EWS
+    assert f(P, big, P, P, PU, ws, None) == EALIGN
+
+
 def test_tensor_quant_noalloc_argument_errors(L):
     f = L.fp8_amax_quant_tensor_noalloc
     assert f(None, 10, P, P, None) == ENULL

@@ -51,3 +51,19 @@ def test_decode_fused_and_per_tensor_lines():
     d = bench("--workload", "c2", "--M", "64", "--steps", "20", "--warmup", "5", "--no-cpu-baseline")
     check_common(d, 20)
     assert d["unit"] == "GB/s"
+
+
+def test_default_line_carries_every_workload():
+    # the default (large-M) line with the other workloads' figures under
+    # "configs", as the full test run records it
+    d = bench("--steps", "5", "--warmup", "2", "--no-cpu-baseline")
+    check_common(d, 5)
+    c = d["configs"]
+    assert set(c) == {"c1", "c2", "c3", "c4"}
+    assert set(c["c2"]) == {f"M={m}" for m in (1, 64, 256, 1024, 65536)}
+    for r in c["c2"].values():
+        assert {"amax_quant_tensor", "amax_tensor"} <= set(r["stages"]) and r["b200_amax_us_context"] > 0
+    assert set(c["c3"]) == {f"M={m}" for m in (1, 8, 32, 64)}
+    for r in c["c3"].values():
+        assert r["two_calls"]["roofline"]["bound"] == "hbm" and "fused_call" in r
+    assert c["c4"]["roofline"]["bound"] == "mfma" and 0 < c["c4"]["roofline"]["frac"] < 1

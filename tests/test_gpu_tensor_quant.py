@@ -1,5 +1,6 @@
 """GPU parity of the per-tensor quantizer (exact amax over the whole tensor):
-bit-exact bytes and scale against the oracle, through the C ABI."""
+bit-exact bytes and scale against the oracle, through the C ABI; the amax
+stage alone (fp8_amax_tensor) gives the exact maximum and the same scale."""
 import numpy as np
 import pytest
 import torch
@@ -23,6 +24,12 @@ def check_tensor(bits, label):
     gq = to_u8(q)
     bad = np.argwhere(gq != q_ref)
     assert bad.shape[0] == 0, (label, bad[:5].tolist())
+    # the amax stage alone (fp8_amax_tensor): the exact maximum and the same scale
+    amax, s2 = fb.fp8_amax_tensor(bf16_to_dev(bits))
+    torch.cuda.synchronize()
+    want = np.float32(np.max(np.abs(synth.bf16_bits_to_f64(bits))))
+    assert to_f32(amax).view(np.uint32)[0] == want.view(np.uint32), (label, to_f32(amax)[0], want)
+    assert to_f32(s2).view(np.uint32)[0] == np.float32(s_ref).view(np.uint32), label
 
 
 @pytest.mark.parametrize("M", [1, 64, 256, 1024, 65536])
