@@ -188,7 +188,21 @@ __global__ __launch_bounds__(kThreads) void weight_quant_block_kernel(
 constexpr int64_t kSmallNumel = 1 << 14;
 constexpr int kMaxPartials = 1024;
 constexpr int kSmallThreads = 1024;
-constexpr int kVecPerThread = 4;  // uint4 (8 bf16) per thread per iteration
+constexpr int kVecPerThread = 4;  // uint4 (8 bf16) per thread per iteration of the amax pass
+// uint4 per thread per iteration of the apply pass (the codes' stores follow
+// each iteration's loads; amax and apply passes over 256 MiB: 113.4 us with
+// 2 in flight, 114.9 with 4)
+constexpr int kApplyVec = 2;
+
+// A load that marks its cache lines as streamed (read once). The amax stage
+// alone uses it (45.4 against 47.8 us over 256 MiB); the quantization's first
+// pass does not, because its second pass re-reads the tensor and finds part
+// of it in the last-level cache only if the first pass left it there.
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ float tail_absmax(const uint16_t* x, int64_t begin, int64_t end, float m) {
   for (int64_t i = begin; i < end; ++i)
@@ -235,20 +249,20 @@ __device__ __forceinline__ void store_nt(uint2 v, uint2* p) {
   __builtin_nontemporal_store(w, reinterpret_cast<u32x2_nt*>(p));
 }
 
-// the same with kVecPerThread vectors per thread in flight, the codes
+// the same with kApplyVec vectors per thread in flight, the codes
 // stored non-temporally, and the tensor walked from its end: the first pass
 // walked it from the start, so the last-level cache holds its most recently
 // read part, which this pass then reads first (when the input is larger
 // than that cache, a walk in the same order would find every line evicted)
-// pre: the thread's first kVecPerThread vectors (i = first + j*stride),
+// pre: the thread's first kApplyVec vectors (i = first + j*stride),
 // loaded by the caller (each index clamped to the tensor, so the loads are
 // unconditional); those past the end are not stored
 template <bool kFast>
 __device__ __forceinline__ void quant_range_nt(const uint4* xv, uint2* qv, int64_t nvec,
                                                 int64_t first, int64_t stride, float s, float r,
-                                                bool zero, const uint4 (&pre)[kVecPerThread]) {
+                                                bool zero, const uint4 (&pre)[kApplyVec]) {
 #pragma unroll
-  for (int j = 0; j < kVecPerThread; ++j) {
+  for (int j = 0; j < kApplyVec; ++j) {
     const int64_t i = first + j * stride;
     if (i < nvec) {
       uint2 o = quant8<kFast>(pre[j], s, r);
@@ -256,13 +270,13 @@ __device__ __forceinline__ void quant_range_nt(const uint4* xv, uint2* qv, int64
       store_nt(o, qv + nvec - 1 - i);
     }
   }
-  int64_t i = first + kVecPerThread * stride;
-  for (; i + (kVecPerThread - 1) * stride < nvec; i += kVecPerThread * stride) {
-    uint4 v[kVecPerThread];
+  int64_t i = first + kApplyVec * stride;
+  for (; i + (kApplyVec - 1) * stride < nvec; i += kApplyVec * stride) {
+    uint4 v[kApplyVec];
 #pragma unroll
-    for (int j = 0; j < kVecPerThread; ++j) v[j] = xv[nvec - 1 - (i + j * stride)];
+    for (int j = 0; j < kApplyVec; ++j) v[j] = xv[nvec - 1 - (i + j * stride)];
 #pragma unroll
-    for (int j = 0; j < kVecPerThread; ++j) {
+    for (int j = 0; j < kApplyVec; ++j) {
       uint2 o = quant8<kFast>(v[j], s, r);
       if (zero) o = make_uint2(0u, 0u);
       store_nt(o, qv + nvec - 1 - (i + j * stride));
@@ -306,6 +320,7 @@ __global__ __launch_bounds__(kSmallThreads) void tensor_quant_small_kernel(
   if (threadIdx.x == 0) scale[0] = s;
 }
 
+template <bool kStream>
 __global__ __launch_bounds__(kThreads) void tensor_amax_partial_kernel(
     const uint16_t* __restrict__ x, float* __restrict__ partial, int64_t numel) {
   __shared__ float lds[kThreads / 64];
@@ -317,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void tensor_amax_partial_kernel(
   for (; i + (kVecPerThread - 1) * stride < nvec; i += kVecPerThread * stride) {
     uint4 v[kVecPerThread];
 #pragma unroll
-    for (int j = 0; j < kVecPerThread; ++j) v[j] = xv[i + j * stride];
+    for (int j = 0; j < kVecPerThread; ++j) v[j] = kStream ? load_nt(xv + i + j * stride) : xv[i + j * stride];
 #pragma unroll
     for (int j = 0; j < kVecPerThread; ++j) {
       m = absmax2(v[j].x, m); m = absmax2(v[j].y, m);
@@ -347,9 +362,9 @@ __global__ __launch_bounds__(kThreads) void tensor_apply_kernel(
   // quantization needs first). Unconditional loads at clamped indices: a
   // conditional one would be sunk by the compiler to its use, after the
   // partials.
-  uint4 pre[kVecPerThread];
+  uint4 pre[kApplyVec];
 #pragma unroll
-  for (int j = 0; j < kVecPerThread; ++j) {
+  for (int j = 0; j < kApplyVec; ++j) {
     const int64_t idx = nvec - 1 - (first + j * stride);
     pre[j] = xv[idx > 0 ? idx : 0];
   }
@@ -592,7 +607,7 @@ int amax_quant_tensor_launch(const void* x_bf16, int64_t numel, void* q_e4m3, fl
     return launch_status();
   }
   const int g = tensor_grid(numel, dev.num_cus);
-  hipLaunchKernelGGL(tensor_amax_partial_kernel, dim3(g), dim3(kThreads), 0, st, x, partial,
+  hipLaunchKernelGGL(tensor_amax_partial_kernel<false>, dim3(g), dim3(kThreads), 0, st, x, partial,
                      numel);
   if (hipGetLastError() != hipSuccess) return FP8BS_ERR_LAUNCH;
   const int64_t nvec = (numel >> 3) + 1;
@@ -681,7 +696,7 @@ int fp8_amax_tensor(const void* x_bf16, int64_t numel, float* amax, float* scale
   }
   float* partial = static_cast<float*>(workspace);
   const int g = tensor_grid(numel, dev.num_cus);
-  hipLaunchKernelGGL(tensor_amax_partial_kernel, dim3(g), dim3(kThreads), 0, st, x, partial, numel);
+  hipLaunchKernelGGL(tensor_amax_partial_kernel<true>, dim3(g), dim3(kThreads), 0, st, x, partial, numel);
   if (hipGetLastError() != hipSuccess) return FP8BS_ERR_LAUNCH;
   hipLaunchKernelGGL(tensor_amax_final_kernel, dim3(1), dim3(kThreads), 0, st, partial, g, amax, scale);
   return launch_status();
