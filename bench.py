@@ -276,7 +276,10 @@ class Workload:
 
 def time_steps(torch, wl, steps, warmup, graph):
     """Warm up, then time exactly `steps` steps between two HIP events on the
-    launch stream (torch's current stream, where the library enqueues). Then,
+    launch stream (torch's current stream, where the library enqueues); one
+    more untimed step is queued just before the start event so that the host's
+    launch of the timed steps does not leave the GPU idle inside the timed
+    region (the region still holds exactly `steps` steps). Then,
     for the per-stage figures, time `steps` back-to-back launches of each
     stage alone the same way (average duration per launch), after a pass that
     gives the spread: each launch between its own pair of events, or, with
@@ -305,6 +308,11 @@ def time_steps(torch, wl, steps, warmup, graph):
         torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    # the last warm-up step is queued right before the start event, so that
+    # the GPU is busy while the host launches the timed steps (a graph launch
+    # takes the host a few hundred microseconds before its first kernel runs)
+    for _, fn, _, _ in wl.stages:
+        fn(warmup)
     e0, e1 = ev(), ev()
     e0.record(st)
     if g is not None:
@@ -312,7 +320,7 @@ def time_steps(torch, wl, steps, warmup, graph):
     else:
         for i in range(steps):
             for _, fn, _, _ in wl.stages:
-                fn(warmup + i)
+                fn(warmup + 1 + i)
     e1.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -337,6 +345,7 @@ def time_steps(torch, wl, steps, warmup, graph):
         if gs is not None:
             reps = []
             for _ in range(10):
+                fn(0)                      # queued in front, as for the steps
                 a, b = ev(), ev()
                 a.record(st)
                 gs.replay()
@@ -353,6 +362,7 @@ def time_steps(torch, wl, steps, warmup, graph):
             reps = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
         spread = (float(np.median(reps)), float(np.percentile(reps, 10)), float(np.percentile(reps, 90)))
         # the average: back-to-back launches between one pair of events
+        fn(0)
         a, b = ev(), ev()
         a.record(st)
         if gs is not None:
@@ -548,6 +558,7 @@ def main():
                 + (", >= 512 MiB of distinct inputs)" if args.rotate == 0 else ")"),
         "config": None,
         "timing": ("step: HIP events around all steps" + (" (HIP graph replay)" if args.graph else "")
+                   + ", the last warm-up step queued just before the start event"
                    + "; stages: HIP events around back-to-back launches of each stage"
                    + (" (each stage replayed from a graph of its own)" if args.graph else "")
                    + "; us_median/p10/p90: " + ("over ten replays of the stage's graph" if args.graph
