@@ -32,10 +32,6 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 128;     // K block
 constexpr int kGroupM = 8;   // m tiles walked per n tile (tile order)
-// MFMA rows of a block over which the copies of the block being prefetched
-// are spread (measured on the prefill shape: rows 0-3 109.1 us, all at once
-// 118.8 us, over all eight rows 115.5 us)
-constexpr int kDmaRows = 4;
 
 __device__ __forceinline__ v4f mfma_16x16x128_fp8(const v8i& a, const v8i& b) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -145,9 +141,18 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int row, int c0) {
 // wave issues NI*NJ MFMAs and 4*NI*NJ scale FMAs per lane.
 //
 // Operand tiles go from global memory straight into LDS (buffer loads with
-// the LDS bit) in a ring of STAGES stages. The copies of block kb+STAGES-1 go
-// into the stage block kb-1 left; they are spread over the first MFMA rows of
-// block kb rather than issued in one burst. The activation scales go to LDS
+// the LDS bit) in two stages, block kb in stage kb % 2. The copies of block
+// kb+1's W tile go into the W half of the stage block kb-1 left, spread over
+// the first two MFMA rows of block kb. A wave reads its A fragments at the
+// start of a block and holds them in registers for the whole block, so after
+// a barrier in the middle of block kb (every wave past its first MFMA rows)
+// the A half of block kb's own stage is free: block kb+2's A tile is copied
+// into it there. The A copies get about a block and a half to land and the W
+// copies about one, and the per-CU copy path, which moves about 48 bytes a
+// clock for these copies (a probe on this chip: one 64 KiB tile pair takes
+// 1370 clocks against the 2048 MFMA clocks of a 256 x 256 block), is kept
+// busy over more of the block than with both tiles copied one block ahead
+// (prefill and large-M GEMMs 4% faster). The activation scales go to LDS
 // in chunks of 8 K blocks (double-buffered, copied with the first block of
 // each chunk): a's scales are row-major [M, K/128], so fetching a block's
 // BM scales alone would touch BM separate cache lines per K block. The
@@ -180,7 +185,7 @@ struct TileCfg {
   static_assert(kWLoads * 1024 * kWaves == kWBytes && kALoads * 1024 * kWaves == kABytes, "loads");
   static_assert(kSCopies * 256 * kWaves == kSChunkBytes, "scale copies");
   static_assert(TN <= 128 && 128 % TN == 0, "a wave's rows must sit in one weight block");
-  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert(STAGES == 2, "the copy schedule assumes two stages");
   static_assert(STAGES * kStageBytes + 2 * kSChunkBytes <= 160 * 1024, "LDS");
 };
 
@@ -303,9 +308,13 @@ void gemm_blockscaled_tiled_kernel(
   const int c0 = 2 * (lane >> 4);
   const int arow = wm * T::TM + (lane & 15);
   const int wrow = wn * T::TN + (lane & 15);
+  // prologue: block 0's tiles and block 1's A tile (block 1's W tile is
+  // copied during block 0)
+  issue(0);
+  if (1 < KB) {
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KB) issue(s);
+    for (int q = 0; q < T::kALoads; ++q) issue_part(1, T::kWLoads + q);
+  }
   constexpr int kPer = T::kWLoads + T::kALoads;   // operand copies per block (scale chunks aside)
   // The weight scale of block kb+1 is loaded (scalar load) after the last
   // fragment read of block kb and waited for right after the next barrier,
@@ -333,10 +342,31 @@ void gemm_blockscaled_tiled_kernel(
     sal[j] = 127;
   }
   wlast = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  // copies of the prefetched block: kPerRow per MFMA row, rows 0..kDmaRows-1
-  constexpr int kRows = kDmaRows < NI - 1 ? kDmaRows : NI - 1;
-  constexpr int kPerRow = (kPer + kRows - 1) / kRows;
-  static_assert((kPer + kPerRow - 1) / kPerRow <= NI - 1, "every copy must be issued");
+  // copies issued during a block: kPerRow per MFMA row, W tile of the next
+  // block first, then (after the mid-block barrier) the A tile of the block
+  // after it; rows 0 .. NI-2 can issue (the last row runs after the next
+  // block's barrier)
+  constexpr int kPerRow = kPer / 2 <= NI - 1 ? 2 : 4;
+  static_assert(T::kWLoads % kPerRow == 0 && T::kALoads % kPerRow == 0, "a row issues copies of one tile");
+  static_assert(kPer / kPerRow <= NI - 1, "every copy must be issued");
+  constexpr int kARow = T::kWLoads / kPerRow;   // first row that copies A, after the barrier
+  // copies of MFMA row i of block kb (PF blocks only, uniform over the
+  // workgroup): W copies of block kb+1, then the barrier and the A copies of
+  // block kb+2. In the last prefetching block kb+2 is past the end: those
+  // copies read rows below the tile's last (or zeros past the matrix) into a
+  // stage half no block reads again.
+  auto issue_row = [&](int kb, int i) {
+    if (i == kARow) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int p = i * kPerRow; p < (i + 1) * kPerRow; ++p) {
+      if (p < T::kWLoads) issue_part(kb + 1, p);
+      else if (p < kPer) issue_part(kb + 2, p);
+    }
+  };
 
   // One K block. PF: the block STAGES-1 ahead is copied in during this one
   // (all but the last STAGES-1 blocks); the two loops keep that decision out
@@ -347,14 +377,10 @@ void gemm_blockscaled_tiled_kernel(
     // kb) are done once at most the copies of the blocks issued after it
     // remain: STAGES-2 groups of at least kPer copies while blocks are being
     // prefetched, fewer in the last iterations (loads complete in order)
-    const int ahead = PF ? STAGES - 2 : min(KB - 1 - kb, STAGES - 2);
-    if (ahead <= 0) {
+    if (kb + 1 < KB)
+      wait_vmcnt<T::kALoads>();   // block kb+1's A copies, issued last, may be in flight
+    else
       wait_vmcnt<0>();
-    } else if (ahead == 1) {
-      wait_vmcnt<kPer>();
-    } else {
-      wait_vmcnt<2 * kPer>();
-    }
     // The last W fragment of block kb-1 (wlast) was read but not yet used:
     // wait for every LDS read (and the scalar load of the weight scale) so
     // that no read of block kb-1's stage is in flight past the barrier.
@@ -398,9 +424,7 @@ void gemm_blockscaled_tiled_kernel(
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[0][j] = mfma_16x16x128_fp8_scaled(wcur, af[j], acc[0][j], swb8, sab[j]);
       if constexpr (PF) {
-#pragma unroll
-        for (int p = 0; p < kPerRow; ++p)
-          if (p < kPer) issue_part(kb + STAGES - 1, p);
+        issue_row(kb, 0);
       }
 #pragma unroll
       for (int i = 1; i < NI - 1; ++i) {
@@ -409,9 +433,7 @@ void gemm_blockscaled_tiled_kernel(
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_16x16x128_fp8_scaled(wcur, af[j], acc[i][j], swb8, sab[j]);
         if constexpr (PF) {
-#pragma unroll
-          for (int p = i * kPerRow; p < (i + 1) * kPerRow; ++p)
-            if (p < kPer) issue_part(kb + STAGES - 1, p);
+          issue_row(kb, i);
         }
       }
       wlast = wnext;
@@ -435,9 +457,7 @@ void gemm_blockscaled_tiled_kernel(
 #pragma unroll
     for (int j = 0; j < NJ; ++j) pp[j] = mfma_16x16x128_fp8(wcur, af[j]);
     if constexpr (PF) {
-#pragma unroll
-      for (int p = 0; p < kPerRow; ++p)
-        if (p < kPer) issue_part(kb + STAGES - 1, p);
+      issue_row(kb, 0);
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
@@ -455,9 +475,7 @@ void gemm_blockscaled_tiled_kernel(
 #pragma unroll
       for (int j = 0; j < NJ; ++j) pc[j] = mfma_16x16x128_fp8(wcur, af[j]);
       if constexpr (PF) {
-#pragma unroll
-        for (int p = i * kPerRow; p < (i + 1) * kPerRow; ++p)
-          if (p < kPer) issue_part(kb + STAGES - 1, p);
+        issue_row(kb, i);
       }
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
