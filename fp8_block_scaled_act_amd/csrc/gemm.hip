@@ -259,9 +259,17 @@ void gemm_blockscaled_tiled_kernel(
   // (past the buffer) and are never used.
   // (kSCopies is even, so copy q's rows have bit 3 equal to q's parity)
   static_assert(T::kSCopies % 2 == 0, "scale copies per wave");
-  const uint32_t srow = static_cast<uint32_t>((wave * T::kSCopies * 8 + (lane >> 3)) * KB * 4);
-  const uint32_t soff[2] = {srow + static_cast<uint32_t>(((lane & 7) ^ sfold(lane >> 3)) * 4),
-                            srow + static_cast<uint32_t>(((lane & 7) ^ sfold(8 + (lane >> 3))) * 4)};
+  // The two per-lane offsets are recomputed at each chunk (every eighth
+  // block) from a lane id the compiler cannot hoist: kept live across the K
+  // loop they pushed the power-of-two kernel over its registers, and the
+  // spill's reload waited for every copy in flight.
+  auto scale_offsets = [&](uint32_t* so) {
+    int ln = static_cast<int>(threadIdx.x & 63);
+    asm volatile("" : "+v"(ln));
+    const uint32_t srow = static_cast<uint32_t>((wave * T::kSCopies * 8 + (ln >> 3)) * KB * 4);
+    so[0] = srow + static_cast<uint32_t>(((ln & 7) ^ sfold(ln >> 3)) * 4);
+    so[1] = srow + static_cast<uint32_t>(((ln & 7) ^ sfold(8 + (ln >> 3))) * 4);
+  };
   // wave-uniform: the weight-scale row address stays in scalar registers
   const int64_t nb = min<int64_t>((n0 + wn * T::TN) / 128, N / 128 - 1);
   const float* swrow = sw + nb * KB;
@@ -288,6 +296,8 @@ void gemm_blockscaled_tiled_kernel(
         const int c = kb / T::kSChunk;
         const v4i_rsrc sr = make_rsrc(stile + c * T::kSChunk, static_cast<uint32_t>(arows * KB * 4 - c * T::kSChunk * 4));
         const uint32_t sd = lds0 + STAGES * T::kStageBytes + (c & 1) * T::kSChunkBytes + wave * T::kSCopies * 256;
+        uint32_t soff[2];
+        scale_offsets(soff);
 #pragma unroll
         for (int q = 0; q < T::kSCopies; ++q)
           copy4_buf_to_lds(soff[q & 1] + static_cast<uint32_t>(q * 8 * KB * 4), sr, sd + q * 256);
