@@ -569,7 +569,7 @@ void gemm_blockscaled_tiled_kernel(
 // ---------------------------------------------------------------------------
 // Decode kernels. At decode shapes the GEMM is bound by streaming W from HBM.
 //
-// Small M (M <= 16): a workgroup takes R W rows over the whole of K, sixteen
+// Small M (M <= 8): a workgroup takes R W rows over the whole of K, sixteen
 // waves; the waves split K into steps of P K blocks (P = 16 / R), wave w
 // taking steps w, w+16, w+32, ... and keeping kDecDepth of them in flight,
 // W fragments and A fragments loaded straight from global memory into
@@ -577,9 +577,10 @@ void gemm_blockscaled_tiled_kernel(
 // scale FMAs. The sixteen waves' partial sums are added through LDS in a
 // fixed order, so the result is deterministic and no second kernel or
 // workspace is needed. Every workgroup reads all of A (through L2), which
-// costs little while A is at most 16 rows. (Staging A in LDS before the K
+// costs little while A is at most 8 rows. (Staging A in LDS before the K
 // loop, as the fused kernel below does with the quantized X, measured
-// slower for every M: 5.8 against 5.4 us at M = 1 with packed blocks.)
+// slower here: 5.8 against 5.4 us at M = 1 with packed blocks; past M = 8
+// the kernel that streams A through LDS in chunks takes over.)
 //
 // Packed K blocks (P > 1, for M <= R): a 16x16 MFMA tile has 16 W rows, but
 // with R = 16 / P W rows per workgroup the grid has P times as many
@@ -595,11 +596,10 @@ void gemm_blockscaled_tiled_kernel(
 // group is its own column's.
 // ---------------------------------------------------------------------------
 constexpr int kDecWaves = 16;
-constexpr int kDecStreamMaxM = 16;
-// K blocks packed into one MFMA for a small-M decode GEMM (rows per
-// workgroup 16 / P must hold the M activation rows)
+// K blocks packed into one MFMA (rows per workgroup 16 / P must hold the M
+// activation rows): the streaming kernel takes M <= 8 with two
 constexpr int kDecPackMaxM = 8;
-inline int decode_pack(int64_t M) { return M <= kDecPackMaxM ? 2 : 1; }
+constexpr int kDecStreamMaxM = kDecPackMaxM;
 
 // Sum over each row of 16 lanes by DPP lane swaps: pairs i^1 and i^2 (quad
 // permutations), then the mirror images within 8 and within 16 lanes. Each
@@ -658,17 +658,13 @@ __device__ __forceinline__ void decode_store(const float4* red, int M, int64_t n
 }
 
 // P: K blocks packed per MFMA (M <= 16 / P); kDecDepth: steps in flight per
-// wave; TS: one scale per tensor (sa[0] * sw[0] for every block); HALF (with
-// P = 1, for 8 < M <= 16): 8 W rows per workgroup, so that every CU streams
-// W here too, the MFMA's rows 8..15 carrying zeros (N = 2048, K = 7168:
-// 8.8 / 9.7 / 10.7 -> 7.7 / 8.6 / 9.5 us at M = 9 / 12 / 16)
-template <int P, int kDecDepth, bool TS, bool HALF = false>
+// wave; TS: one scale per tensor (sa[0] * sw[0] for every block)
+template <int P, int kDecDepth, bool TS>
 __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(kDecWaves / 4, kDecWaves / 4)))
 void gemm_blockscaled_decode_stream_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, uint16_t* __restrict__ C, int M, int64_t N, int64_t K) {
-  static_assert(!HALF || P == 1, "half tiles take one K block per step");
-  constexpr int R = HALF ? 8 : 16 / P;
+  constexpr int R = 16 / P;
   __shared__ float4 red[kDecWaves * 64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -677,14 +673,12 @@ void gemm_blockscaled_decode_stream_kernel(
 
   // lane l supplies W row n0 + rsub and A row rsub (rows past M read row
   // M-1: valid memory, results never stored) of K block P*s + grp of step s,
-  // bytes 32*(l/16) ..+32 of the block; HALF: W row n0 + l%8 from lanes with
-  // l%16 < 8 (zeros from the others), A row l%16
-  const int rsub = HALF ? (lane & 7) : (lane & 15) % R;
-  const int grp = HALF ? 0 : (lane & 15) / R;
-  const bool wuse = !HALF || (lane & 15) < 8;
+  // bytes 32*(l/16) ..+32 of the block
+  const int rsub = (lane & 15) % R;
+  const int grp = (lane & 15) / R;
   const int koff = 32 * (lane >> 4);
   const uint8_t* wp = W + (n0 + rsub) * K + koff;
-  const int64_t am = min(HALF ? (lane & 15) : rsub, M - 1);
+  const int64_t am = min<int64_t>(rsub, M - 1);
   const uint8_t* ap = A + am * K + koff;
   const float* sp = sa + am * KB;
   const float* swrow = sw + (n0 / 128) * KB;
@@ -700,12 +694,8 @@ void gemm_blockscaled_decode_stream_kernel(
   auto load = [&](int d, int t) {
     const int64_t kb = static_cast<int64_t>(wave + kDecWaves * t) * P + grp;
     if (P == 1 || kb < KB) {
-      if (wuse) {
-        wq[d][0] = *reinterpret_cast<const uint4*>(wp + kb * kBK);
-        wq[d][1] = *reinterpret_cast<const uint4*>(wp + kb * kBK + 16);
-      } else {
-        wq[d][0] = wq[d][1] = make_uint4(0, 0, 0, 0);
-      }
+      wq[d][0] = *reinterpret_cast<const uint4*>(wp + kb * kBK);
+      wq[d][1] = *reinterpret_cast<const uint4*>(wp + kb * kBK + 16);
       aq[d][0] = *reinterpret_cast<const uint4*>(ap + kb * kBK);
       aq[d][1] = *reinterpret_cast<const uint4*>(ap + kb * kBK + 16);
       if constexpr (!TS) sq[d] = sp[kb];
@@ -749,12 +739,8 @@ void gemm_blockscaled_decode_stream_kernel(
 template <bool TS>
 int launch_decode_stream(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c,
                          int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  if (decode_pack(M) == 2)
-    hipLaunchKernelGGL((gemm_blockscaled_decode_stream_kernel<2, 4, TS>), dim3(static_cast<unsigned>(N / 8)),
-                       dim3(64 * kDecWaves), 0, st, a, sa, w, sw, c, static_cast<int>(M), N, K);
-  else
-    hipLaunchKernelGGL((gemm_blockscaled_decode_stream_kernel<1, 4, TS, true>), dim3(static_cast<unsigned>(N / 8)),
-                       dim3(64 * kDecWaves), 0, st, a, sa, w, sw, c, static_cast<int>(M), N, K);
+  hipLaunchKernelGGL((gemm_blockscaled_decode_stream_kernel<2, 4, TS>), dim3(static_cast<unsigned>(N / 8)),
+                     dim3(64 * kDecWaves), 0, st, a, sa, w, sw, c, static_cast<int>(M), N, K);
   return FP8BS_OK;
 }
 
@@ -934,7 +920,7 @@ int launch_act_quant_gemm_decode(const void* x, const uint8_t* w, const float* s
 }
 
 // ---------------------------------------------------------------------------
-// Larger decode M (16 < M <= 64): the work is cut into many pieces of W so
+// Larger decode M (32 < M <= 64): the work is cut into many pieces of W so
 // that A is shared: workgroup (n tile of 64 rows, K split)
 // has four waves, wave w owning W rows 16w..16w+15 of the tile. Each wave
 // loads its W fragments straight from global memory into registers
@@ -1168,11 +1154,11 @@ int launch_decode(const uint8_t* a, const float* sa, const uint8_t* w, const flo
   if (p.kb_per <= 4) FP8BS_DEC(MT, 4);        \
   else if (p.kb_per <= 8) FP8BS_DEC(MT, 8);   \
   else FP8BS_DEC(MT, 16);
-  switch (mt) {
-    case 1: FP8BS_DEC_KB(1) break;
-    case 2: FP8BS_DEC_KB(2) break;
-    case 3: FP8BS_DEC_KB(3) break;
-    default: FP8BS_DEC_KB(4) break;
+  // M > 32 here (smaller M takes the kernels above)
+  if (mt <= 3) {
+    FP8BS_DEC_KB(3)
+  } else {
+    FP8BS_DEC_KB(4)
   }
 #undef FP8BS_DEC_KB
 #undef FP8BS_DEC
@@ -1182,6 +1168,222 @@ int launch_decode(const uint8_t* a, const float* sa, const uint8_t* w, const flo
     hipLaunchKernelGGL(gemm_splitk_reduce_kernel, dim3(static_cast<unsigned>((mn4 + 255) / 256)), dim3(256), 0, st,
                        ws, c, mn4, p.splits);
   }
+  return FP8BS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Decode with A staged through LDS (8 < M <= 32). A workgroup takes 8 W rows
+// over the whole of K with sixteen waves, as the streaming kernel does, but
+// both operands reach it through the per-CU copy path in that path's
+// efficient form: 1 KiB copies (eight rows of 128 bytes, buffer loads with
+// the LDS bit) of chunks of CB K blocks, two chunks in flight. Fragment loads
+// straight into registers touch sixteen half-used 128-byte lines per
+// instruction and left the streaming kernel bound by A's loads once M passed
+// 8. Wave w takes the K blocks kb = w (mod 16): per block, one MFMA per 16
+// activation rows (the MFMA's W rows 8..15 repeat rows 0..7, and those
+// outputs are dropped), then the scale FMAs. The sixteen waves' partial sums
+// are added through LDS in wave order: deterministic, one launch, no
+// workspace. Every global load of the kernel is one of these copies, so the
+// kernel alone counts them when it waits. (N = 2048, K = 7168: M = 12 / 16 /
+// 24 / 32 in 7.0 / 7.2 / 9.0 / 9.1 us, against 8.7 / 9.6 / 9.8 / 10.0 us
+// with the streaming kernel or the split-K kernel and its reduce. Past
+// M = 32 every CU would read more of A than of W, and the split-K kernel is
+// faster: 13.3 against 11.0 us at M = 48.)
+// ---------------------------------------------------------------------------
+constexpr int kFullMaxM = 32;
+constexpr int kFullWaves = 16;
+constexpr int kFullRows = 8;
+template <int MT>
+struct FullCfg {
+  static constexpr int MP = 16 * MT;                    // A rows staged (M rounded up to 16)
+  static_assert(MT == 1 || MT == 2, "M <= 32");
+  static constexpr int CB = MT == 1 ? 16 : 8;           // K blocks per chunk
+  static constexpr int NBUF = 3;                        // chunk buffers (two chunks in flight)
+  static constexpr int kAChunk = MP * CB * 128;         // A bytes per chunk
+  static constexpr int kWChunk = kFullRows * CB * 128;  // W bytes per chunk
+  static constexpr int kSChunk = (MP * CB * 4 + 1023) / 1024 * 1024;   // activation scales per chunk (padded to 1 KiB)
+  static constexpr int kChunk = kAChunk + kWChunk + kSChunk + 256;   // + the weight scales
+  static constexpr int kSCopies4 = MP * CB * 4 / 256;        // 256-byte scale copies per chunk
+  static constexpr int kSRows16 = 256 / CB;                   // rows one 1 KiB scale copy covers
+  static_assert(CB <= kFullWaves && MP * CB * 4 % 256 == 0 && kSCopies4 <= kFullWaves && MP <= kSRows16, "copies");
+  static_assert(kFullWaves * MT * 64 * 16 <= NBUF * kChunk, "the waves' partial sums fit the chunk buffers");
+  static_assert(NBUF * kChunk <= 160 * 1024, "LDS");
+};
+
+// SC16: the activation scales go in one 1 KiB copy per chunk (rows of K/128
+// floats 16-byte aligned: K/128 a multiple of 4), else in 256-byte copies
+template <int MT, bool TS, bool SC16>
+__global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
+    const float* __restrict__ sw, uint16_t* __restrict__ C, int M, int64_t N, int64_t K) {
+  using F = FullCfg<MT>;
+  constexpr int MP = F::MP, CB = F::CB;
+  // NBUF chunk buffers, each [A: CB blocks x MP rows x 128][W: CB blocks x 8
+  // rows x 128][activation scales: MP x CB][weight scales: CB]
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[F::NBUF * F::kChunk];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kFullRows;
+  const int KB = static_cast<int>(K / kBK);
+  const int nchunks = (KB + CB - 1) / CB;
+  const uint32_t lds0 = lds_addr(lds);
+
+  // Copies of chunk c: kTot copies, copy k issued by wave k % 16 (no copy is
+  // issued twice: each copy instruction costs the copy path about the same
+  // whatever its size, and repeating the small scale copies in every wave
+  // cost 2-3 us per call at M = 64):
+  // - A copy k < kACopies covers K block k / (MP/8) of the chunk and rows
+  //   8 (k % (MP/8)) .. +7; lane l fetches row r = 8 (k % (MP/8)) + l/8, the
+  //   16-byte piece that the row swizzle puts at LDS position l % 8. Rows at
+  //   or past M read zeros (range-checked buffer).
+  // - W copy: block cb of the chunk, the workgroup's 8 rows.
+  // - activation-scale copies: the chunk's [row][CB] floats, in one 1 KiB
+  //   copy (4 floats a lane) when the rows are 16-byte aligned, else in
+  //   256-byte copies of 64 floats.
+  // - weight-scale copy: the chunk's CB weight scales (the workgroup's 8 rows
+  //   sit in one 128-row block; lanes past CB fetch floats never used).
+  // Blocks past K/128 in the last chunk read the next row or zeros and are
+  // never used.
+  constexpr int kACopies = MP * CB / 8;
+  constexpr int kSCopies = SC16 ? 1 : F::kSCopies4;
+  constexpr int kTot = kACopies + CB + (TS ? 0 : kSCopies + 1);
+  const v4i_rsrc ar = make_rsrc(A, static_cast<uint32_t>(M * K));
+  const v4i_rsrc wr = make_rsrc(W + n0 * K, static_cast<uint32_t>(kFullRows * K));
+  const v4i_rsrc sr = make_rsrc(sa, static_cast<uint32_t>(M * KB * 4));
+  const v4i_rsrc swr = make_rsrc(sw + (n0 / 128) * KB, static_cast<uint32_t>(KB * 4));
+  auto issue_chunk = [&](int c) {
+    const uint32_t base = lds0 + (c % F::NBUF) * F::kChunk;
+    for (int k = wave; k < kTot; k += kFullWaves) {
+      if (k < kACopies) {
+        const int cb = k / (MP / 8);
+        const int r = 8 * (k % (MP / 8)) + (lane >> 3);
+        const uint32_t off = static_cast<uint32_t>(r * K) + static_cast<uint32_t>(c * CB + cb) * kBK +
+                             static_cast<uint32_t>(((lane & 7) ^ swz(r)) << 4);
+        copy16_buf_to_lds(off, ar, base + k * 1024);
+      } else if (k < kACopies + CB) {
+        const int cb = k - kACopies;
+        const int r = lane >> 3;
+        const uint32_t off = static_cast<uint32_t>(r * K) + static_cast<uint32_t>(c * CB + cb) * kBK +
+                             static_cast<uint32_t>(((lane & 7) ^ swz(r)) << 4);
+        copy16_buf_to_lds(off, wr, base + F::kAChunk + cb * 1024);
+      } else if (k < kACopies + CB + kSCopies) {
+        if constexpr (SC16) {
+          const int r = (4 * lane) / CB, x = (4 * lane) % CB;
+          copy16_buf_to_lds(static_cast<uint32_t>((r * KB + c * CB + x) * 4), sr, base + F::kAChunk + F::kWChunk);
+        } else {
+          const int s = k - kACopies - CB;
+          const int e = s * 64 + lane;
+          const int r = e / CB, x = e % CB;
+          copy4_buf_to_lds(static_cast<uint32_t>((r * KB + c * CB + x) * 4), sr,
+                           base + F::kAChunk + F::kWChunk + s * 256);
+        }
+      } else {
+        copy4_buf_to_lds(static_cast<uint32_t>((c * CB + lane) * 4), swr,
+                         base + F::kAChunk + F::kWChunk + F::kSChunk);
+      }
+    }
+  };
+  // this wave's copies per chunk: the first kTot % 16 waves issue one more
+  constexpr int kFew = kTot / kFullWaves, kExtra = kTot % kFullWaves;
+  auto wait_chunks = [&](auto n) {   // all but this wave's copies of the last n chunks issued are done
+    constexpr int kN = decltype(n)::value;
+    if (wave < kExtra)
+      wait_vmcnt<kN * (kFew + 1)>();
+    else
+      wait_vmcnt<kN * kFew>();
+  };
+
+  const float tscale = TS ? sa[0] * sw[0] : 0.0f;
+
+  // chunks 0 .. NBUF-2 now; chunk c + NBUF - 1 right after the barrier that
+  // opens chunk c (every wave is then done with chunk c-1, whose buffer it
+  // refills), so NBUF - 1 chunks stay in flight behind the one computed
+  for (int c = 0; c < F::NBUF - 1; ++c)
+    if (c < nchunks) issue_chunk(c);
+
+  v4f acc[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  const int c0 = 2 * (lane >> 4);
+  for (int c = 0; c < nchunks; ++c) {
+    // chunk c's copies are done once at most those of the chunks issued
+    // after it remain: min(NBUF - 2, nchunks - 1 - c) chunks
+    const int after = min(F::NBUF - 2, nchunks - 1 - c);
+    if (after >= 2)
+      wait_chunks(std::integral_constant<int, 2>{});
+    else if (after == 1)
+      wait_chunks(std::integral_constant<int, 1>{});
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of chunk c-1 are back
+    __builtin_amdgcn_s_barrier();
+    if (c + F::NBUF - 1 < nchunks) issue_chunk(c + F::NBUF - 1);
+    const uint8_t* chunk = lds + (c % F::NBUF) * F::kChunk;
+    const float* ss = reinterpret_cast<const float*>(chunk + F::kAChunk + F::kWChunk);
+    const float* sws = ss + MP * CB;
+    for (int x = (wave - c * CB) & 15; x < CB; x += 16) {
+      const int kb = c * CB + x;
+      if (kb >= KB) break;
+      const float swb = TS ? 1.0f : sws[x];
+      const v8i wf = lds_frag(chunk + F::kAChunk + x * 1024, lane & 7, c0);
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+        const v8i af = lds_frag(chunk + x * MP * 128, j * 16 + (lane & 15), c0);
+        const v4f p = mfma_16x16x128_fp8(wf, af);
+        const float cs = TS ? tscale : ss[(j * 16 + (lane & 15)) * CB + x] * swb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(p[r], cs, acc[j][r]);
+      }
+    }
+  }
+  // every wave is done with the chunk buffers (and no copy is in flight: the
+  // last chunk waited for all of them)
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __syncthreads();
+
+  // the waves' partial sums, [wave][j][lane] float4, over the chunk buffers
+  float4* red = reinterpret_cast<float4*>(lds);
+#pragma unroll
+  for (int j = 0; j < MT; ++j)
+    red[(wave * MT + j) * 64 + lane] = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+  __syncthreads();
+  // thread t < 2M: activation row m = t/2, W rows n0 + 4 (t%2) .. +3, which
+  // lane 16 (t%2) + m%16 of tile m/16 holds in every wave; added in wave order
+  const int t = static_cast<int>(threadIdx.x);
+  if (t < 2 * M) {
+    const int m = t >> 1, q = t & 1;
+    const int l = 16 * q + (m & 15), j = m >> 4;
+    float4 s = red[j * 64 + l];
+    for (int w = 1; w < kFullWaves; ++w) {
+      const float4 u = red[(w * MT + j) * 64 + l];
+      s.x += u.x; s.y += u.y; s.z += u.z; s.w += u.w;
+    }
+    uint2 o;
+    o.x = bf16x2_rne(s.x, s.y);
+    o.y = bf16x2_rne(s.z, s.w);
+    *reinterpret_cast<uint2*>(C + static_cast<int64_t>(m) * N + n0 + 4 * q) = o;
+  }
+}
+
+template <bool TS>
+int launch_decode_full(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c,
+                       int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(N / kFullRows));
+  const int m = static_cast<int>(M);
+  const bool sc16 = TS || (K / kBK) % 4 == 0;
+#define FP8BS_FULL(MT)                                                                                     \
+  if (sc16)                                                                                                 \
+    hipLaunchKernelGGL((gemm_blockscaled_decode_full_kernel<MT, TS, true>), grid, dim3(64 * kFullWaves), 0, st, \
+                       a, sa, w, sw, c, m, N, K);                                                           \
+  else                                                                                                      \
+    hipLaunchKernelGGL((gemm_blockscaled_decode_full_kernel<MT, TS, false>), grid, dim3(64 * kFullWaves), 0, st, \
+                       a, sa, w, sw, c, m, N, K)
+  if (m <= 16) {
+    FP8BS_FULL(1);
+  } else {
+    FP8BS_FULL(2);
+  }
+#undef FP8BS_FULL
   return FP8BS_OK;
 }
 
@@ -1230,7 +1432,7 @@ inline bool gemm_shape_ok(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return false;
   if (M > (INT64_MAX / K) || M > (INT64_MAX / N) || N > (INT64_MAX / K)) return false;
   if (K > (int64_t{1} << 22) || (M + 127) / 128 > 0x7FFFFFFF) return false;
-  if (use_decode(M) && M > kDecStreamMaxM && K / 128 > static_cast<int64_t>(kDecMaxSplits) * kDecMaxKb)
+  if (use_decode(M) && M > kFullMaxM && K / 128 > static_cast<int64_t>(kDecMaxSplits) * kDecMaxKb)
     return false;
   return true;
 }
@@ -1244,7 +1446,7 @@ extern "C" {
 
 size_t fp8_gemm_blockscaled_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (!gemm_shape_ok(M, N, K)) return 0;
-  return use_decode(M) && M > kDecStreamMaxM ? decode_workspace_bytes(M, N, K) : 0;
+  return use_decode(M) && M > kFullMaxM ? decode_workspace_bytes(M, N, K) : 0;
 }
 
 }  // extern "C"
@@ -1275,6 +1477,8 @@ int gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m
   if (use_decode(M)) {
     if (M <= kDecStreamMaxM)
       rc = launch_decode_stream<MODE == 2>(a, a_scale, w, w_scale, c, M, N, K, st);
+    else if (M <= kFullMaxM)
+      rc = launch_decode_full<MODE == 2>(a, a_scale, w, w_scale, c, M, N, K, st);
     else
       rc = launch_decode<MODE == 2>(a, a_scale, w, w_scale, c, static_cast<float*>(workspace), M, N, K, st);
     if (rc != FP8BS_OK) return rc;

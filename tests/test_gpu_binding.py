@@ -33,7 +33,7 @@ def test_act_quant_outputs_checked():
 def test_gemm_out_and_workspace_checked():
     fb = binding()
     say("binding: GEMM out= and workspace checks")
-    d = synth.gen_c3(32)
+    d = synth.gen_c3(48)      # the split-K decode path: a workspace is needed
     qa, sa = quant.act_quant_block(d["a"])
     qw, sw = quant.weight_quant_block(d["w"])
     args = (u8_to_dev(qa), f32_to_dev(sa), u8_to_dev(qw), f32_to_dev(sw))
@@ -53,6 +53,6 @@ def test_gemm_out_and_workspace_checked():
     c2 = fb.fp8_gemm_blockscaled(*args)
     torch.cuda.synchronize()
     assert np.array_equal(to_bf16_bits(c1), to_bf16_bits(c2))
-    if wsb > 8:
-        with pytest.raises(fb.Fp8bsError):      # one int64 too few
-            fb.fp8_gemm_blockscaled(*args, workspace=ws64[: wsb // 8 - 1])
+    assert wsb > 8
+    with pytest.raises(fb.Fp8bsError):      # one int64 too few
+        fb.fp8_gemm_blockscaled(*args, workspace=ws64[: wsb // 8 - 1])
