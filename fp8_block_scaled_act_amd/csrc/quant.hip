@@ -188,7 +188,14 @@ __global__ __launch_bounds__(kThreads) void weight_quant_block_kernel(
 constexpr int64_t kSmallNumel = 1 << 14;
 constexpr int kMaxPartials = 1024;
 constexpr int kSmallThreads = 1024;
-constexpr int kVecPerThread = 4;  // uint4 (8 bf16) per thread per iteration of the amax pass
+// uint4 (8 bf16) per thread per iteration of the amax pass: 4 with up to
+// four workgroups per CU, 8 with one workgroup per CU for inputs whose
+// 4-deep grid would exceed four workgroups per CU (256 MiB: 47.3 -> 40.8 us
+// for the amax stage alone, 110.4 -> 103.7 us for the quantization; 16 Mi
+// elements: 10.1 -> 9.3 / 19.2 -> 17.2 us; below that, fewer and deeper
+// workgroups were slower: 4.2 -> 4.8 us at 131072 elements)
+constexpr int kVecPerThread = 4;
+constexpr int kVecDeep = 8;
 // uint4 per thread per iteration of the apply pass (the codes' stores follow
 // each iteration's loads; amax and apply passes over 256 MiB: 113.4 us with
 // 2 in flight, 114.9 with 4)
@@ -320,7 +327,7 @@ __global__ __launch_bounds__(kSmallThreads) void tensor_quant_small_kernel(
   if (threadIdx.x == 0) scale[0] = s;
 }
 
-template <bool kStream>
+template <bool kStream, int kVec>
 __global__ __launch_bounds__(kThreads) void tensor_amax_partial_kernel(
     const uint16_t* __restrict__ x, float* __restrict__ partial, int64_t numel) {
   __shared__ float lds[kThreads / 64];
@@ -329,12 +336,12 @@ __global__ __launch_bounds__(kThreads) void tensor_amax_partial_kernel(
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
   float m = 0.0f;
   int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  for (; i + (kVecPerThread - 1) * stride < nvec; i += kVecPerThread * stride) {
-    uint4 v[kVecPerThread];
+  for (; i + (kVec - 1) * stride < nvec; i += kVec * stride) {
+    uint4 v[kVec];
 #pragma unroll
-    for (int j = 0; j < kVecPerThread; ++j) v[j] = kStream ? load_nt(xv + i + j * stride) : xv[i + j * stride];
+    for (int j = 0; j < kVec; ++j) v[j] = kStream ? load_nt(xv + i + j * stride) : xv[i + j * stride];
 #pragma unroll
-    for (int j = 0; j < kVecPerThread; ++j) {
+    for (int j = 0; j < kVec; ++j) {
       m = absmax2(v[j].x, m); m = absmax2(v[j].y, m);
       m = absmax2(v[j].z, m); m = absmax2(v[j].w, m);
     }
@@ -456,13 +463,37 @@ int64_t block_tensor_partials(int64_t M, int64_t K) {
   return (M * (K / 128) * 8 + kBTThreads - 1) / kBTThreads;
 }
 
-int tensor_grid(int64_t numel, int num_cus) {
+// Grid of the amax pass (= its number of partial maxima, at most
+// kMaxPartials) and whether it runs the deep form (kVecDeep vectors per
+// thread, one workgroup per CU)
+struct TensorGrid {
+  int g;
+  bool deep;
+};
+TensorGrid tensor_grid(int64_t numel, int num_cus) {
   const int64_t nvec = (numel >> 3) + 1;
   const int64_t per_wg = static_cast<int64_t>(kThreads) * kVecPerThread;
-  int64_t g = (nvec + per_wg - 1) / per_wg;
-  const int64_t cap = std::min<int64_t>(kMaxPartials, 4LL * num_cus);
-  if (g > cap) g = cap;
-  return static_cast<int>(g < 1 ? 1 : g);
+  const int64_t g = (nvec + per_wg - 1) / per_wg;
+  if (g > 4LL * num_cus) return {static_cast<int>(std::min<int64_t>(kMaxPartials, num_cus)), true};
+  return {static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(kMaxPartials, g))), false};
+}
+// Grid of the apply pass: up to 8 workgroups per CU, 4 once each thread
+// would take more than 8 vectors at 8 (256 MiB: 105.7 -> 99.6 us for the
+// quantization; 16 Mi elements: 17.3 against 17.7 us with 8)
+int64_t apply_grid(int64_t numel, int num_cus) {
+  const int64_t nvec = (numel >> 3) + 1;
+  const int64_t ga = (nvec + kThreads * kApplyVec - 1) / (kThreads * kApplyVec);
+  const int64_t per_cu = nvec > 8LL * num_cus * kThreads * 8 ? 4 : 8;
+  return std::min<int64_t>(ga, per_cu * num_cus);
+}
+template <bool kStream>
+void launch_amax_partial(const TensorGrid& tg, const uint16_t* x, float* partial, int64_t numel, hipStream_t st) {
+  if (tg.deep)
+    hipLaunchKernelGGL((tensor_amax_partial_kernel<kStream, kVecDeep>), dim3(tg.g), dim3(kThreads), 0, st, x,
+                       partial, numel);
+  else
+    hipLaunchKernelGGL((tensor_amax_partial_kernel<kStream, kVecPerThread>), dim3(tg.g), dim3(kThreads), 0, st, x,
+                       partial, numel);
 }
 
 // ---------------------------------------------------------------------------
@@ -606,13 +637,11 @@ int amax_quant_tensor_launch(const void* x_bf16, int64_t numel, void* q_e4m3, fl
                        numel);
     return launch_status();
   }
-  const int g = tensor_grid(numel, dev.num_cus);
-  hipLaunchKernelGGL(tensor_amax_partial_kernel<false>, dim3(g), dim3(kThreads), 0, st, x, partial,
-                     numel);
+  const TensorGrid tg = tensor_grid(numel, dev.num_cus);
+  const int g = tg.g;
+  launch_amax_partial<false>(tg, x, partial, numel, st);
   if (hipGetLastError() != hipSuccess) return FP8BS_ERR_LAUNCH;
-  const int64_t nvec = (numel >> 3) + 1;
-  int64_t ga = (nvec + kThreads * 2 - 1) / (kThreads * 2);
-  ga = std::min<int64_t>(ga, 8LL * dev.num_cus);
+  const int64_t ga = apply_grid(numel, dev.num_cus);
   hipLaunchKernelGGL(tensor_apply_kernel, dim3(static_cast<unsigned>(ga)), dim3(kThreads), 0, st, x,
                      q, scale, partial, g, numel);
   return launch_status();
@@ -695,8 +724,9 @@ int fp8_amax_tensor(const void* x_bf16, int64_t numel, float* amax, float* scale
     return launch_status();
   }
   float* partial = static_cast<float*>(workspace);
-  const int g = tensor_grid(numel, dev.num_cus);
-  hipLaunchKernelGGL(tensor_amax_partial_kernel<true>, dim3(g), dim3(kThreads), 0, st, x, partial, numel);
+  const TensorGrid tg = tensor_grid(numel, dev.num_cus);
+  const int g = tg.g;
+  launch_amax_partial<true>(tg, x, partial, numel, st);
   if (hipGetLastError() != hipSuccess) return FP8BS_ERR_LAUNCH;
   hipLaunchKernelGGL(tensor_amax_final_kernel, dim3(1), dim3(kThreads), 0, st, partial, g, amax, scale);
   return launch_status();
@@ -743,9 +773,7 @@ int fp8_act_quant_block_tensor(const void* x_bf16, int64_t M, int64_t K, void* q
                      M * (K / 128));
   if (hipGetLastError() != hipSuccess) return FP8BS_ERR_LAUNCH;
   const int64_t numel = M * K;
-  const int64_t nvec = (numel >> 3) + 1;
-  int64_t ga = (nvec + kThreads * 2 - 1) / (kThreads * 2);
-  ga = std::min<int64_t>(ga, 8LL * dev.num_cus);
+  const int64_t ga = apply_grid(numel, dev.num_cus);
   hipLaunchKernelGGL(tensor_apply_kernel, dim3(static_cast<unsigned>(ga)), dim3(kThreads), 0, st,
                      static_cast<const uint16_t*>(x_bf16), static_cast<uint8_t*>(qt_e4m3), tensor_scale, partial,
                      static_cast<int>(np), numel);
