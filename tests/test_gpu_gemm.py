@@ -44,6 +44,19 @@ def check_full(qa, sa, qw, sw, label, c=None):
     return res
 
 
+def test_unit_scales_2048_cube():
+    # The DeepSeek-V3 page benchmarks its FP8 GEMM kernel at M = N = K = 2048
+    # (section "Benchmarking the FP8 GEMM Kernel"). With every scale 1 the
+    # output is the plain FP8 product of the codes; codes of N(0,1)*60 data
+    rng = np.random.default_rng(2048)
+    enc = lambda shape: e4m3.encode(np.clip(rng.standard_normal(shape) * 60, -448, 448).astype(np.float32))
+    qa = enc((2048, 2048)).astype(np.uint8)
+    qw = enc((2048, 2048)).astype(np.uint8)
+    sa = np.ones((2048, 16), np.float32)
+    sw = np.ones((16, 16), np.float32)
+    check_full(qa, sa, qw, sw, "unit scales 2048x2048x2048")
+
+
 def test_c1_tiny():
     d = synth.gen_c1()
     check_full(*operands(d["a"], d["w"]), "C1 32x512x512")
