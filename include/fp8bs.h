@@ -93,7 +93,8 @@ int fp8_act_quant_block_f32(const float* x_f32, int64_t M, int64_t K,
  *   q_e4m3     [numel] e4m3 bytes, 16-byte aligned  (output)
  *   scale      [1] fp32, 4-byte aligned             (output, written on device)
  *   workspace  device scratch of at least
- *              fp8_amax_quant_tensor_workspace_bytes(numel) bytes, 16-byte
+ *              fp8_amax_quant_tensor_workspace_bytes(numel) bytes (0 when
+ *              numel <= 65536, which one launch serves; 4 KiB above), 16-byte
  *              aligned; may be NULL when that size is 0. Its contents on entry
  *              do not matter; it must not be shared by calls that can run
  *              concurrently.

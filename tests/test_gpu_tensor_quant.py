@@ -41,7 +41,12 @@ def test_c5_activation():
     check_tensor(synth.gen_c5()["a"], "C5 A 16384x2048")
 
 
-@pytest.mark.parametrize("numel", [1, 7, 8, 9, 127, 1000, (1 << 17) - 1, 1 << 17,
+# the three forms: one workgroup (up to 2^14 elements), several workgroups that
+# each read the whole tensor (up to 2^16), two passes (above); sizes on both
+# sides of each switch, ragged tails, shares of the mid form that end early
+@pytest.mark.parametrize("numel", [1, 7, 8, 9, 127, 1000, (1 << 14) - 1, 1 << 14, (1 << 14) + 1,
+                                   (1 << 14) + 8, 20_007, 40_000, (1 << 16) - 3, 1 << 16, (1 << 16) + 1,
+                                   (1 << 16) + 8, (1 << 17) - 1, 1 << 17,
                                    (1 << 17) + 1, (1 << 17) + 7, 1_000_003, 5 * (1 << 20) + 5])
 def test_ragged_numel(numel):
     rng = np.random.default_rng(numel)
@@ -57,7 +62,7 @@ def test_max_in_the_tail():
     check_tensor(synth.f64_to_bf16_bits(x), "max in tail")
 
 
-@pytest.mark.parametrize("numel", [100, (1 << 17) + 9, 3 << 20])
+@pytest.mark.parametrize("numel", [100, 50_001, (1 << 17) + 9, 3 << 20])
 def test_all_zero_and_tiny(numel):
     check_tensor(np.zeros(numel, np.uint16), f"zeros {numel}")
     neg0 = np.full(numel, 0x8000, np.uint16)

@@ -36,6 +36,7 @@ def test_noalloc_equals_workspace_entry_point():
     cases = [("per-tensor sweep M=65536", synth.gen_c2(65536)["x"], 1000.0),
              ("M=1024", synth.gen_c2(1024)["x"], 10.0),
              ("ragged 300001 elements", synth.f64_to_bf16_bits(rng.standard_normal(300001)), 1.0),
+             ("one launch, several workgroups, 40009 elements", synth.f64_to_bf16_bits(rng.standard_normal(40009)), 1.0),
              ("small path 4099 elements", synth.f64_to_bf16_bits(rng.standard_normal(4099)), 1.0)]
     for label, bits, mul in cases:
         x = bf16_to_dev(bits) * mul
