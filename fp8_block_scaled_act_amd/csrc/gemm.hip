@@ -920,9 +920,9 @@ int launch_act_quant_gemm_decode(const void* x, const uint8_t* w, const float* s
 }
 
 // ---------------------------------------------------------------------------
-// Larger decode M (32 < M <= 64): the work is cut into many pieces of W so
-// that A is shared: workgroup (n tile of 64 rows, K split)
-// has four waves, wave w owning W rows 16w..16w+15 of the tile. Each wave
+// Larger decode M with wide W (32 < M <= 64, N > 2048): the work is cut
+// into many pieces of W so that A is shared: workgroup (n tile of 64 rows, K
+// split) has four waves, wave w owning W rows 16w..16w+15 of the tile. Each wave
 // loads its W fragments straight from global memory into registers
 // (kDepth K blocks in flight), the K split's slice of A (at most 64 rows)
 // and its activation scales are staged once in LDS and shared, and each K
@@ -1134,6 +1134,13 @@ inline DecodePlan decode_plan(int64_t N, int64_t K) {
 }
 
 inline bool use_decode(int64_t M) { return M <= kDecMaxM; }
+// The chunked full-K kernel (below) serves 8 < M <= kFullMaxM for every N,
+// and kFullMaxM < M <= 64 while N <= kFull2dMaxN (N / 8 workgroups: one per
+// CU on 256 CUs); the split-K kernel and its reduce serve the rest of
+// 32 < M <= 64.
+constexpr int kFullMaxM = 32;
+constexpr int64_t kFull2dMaxN = 2048;
+inline bool use_split_k(int64_t M, int64_t N) { return use_decode(M) && M > kFullMaxM && N > kFull2dMaxN; }
 
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   const DecodePlan p = decode_plan(N, K);
@@ -1172,35 +1179,48 @@ int launch_decode(const uint8_t* a, const float* sa, const uint8_t* w, const flo
 }
 
 // ---------------------------------------------------------------------------
-// Decode with A staged through LDS (8 < M <= 32). A workgroup takes 8 W rows
-// over the whole of K with sixteen waves, as the streaming kernel does, but
-// both operands reach it through the per-CU copy path in that path's
-// efficient form: 1 KiB copies (eight rows of 128 bytes, buffer loads with
-// the LDS bit) of chunks of CB K blocks, two chunks in flight. Fragment loads
-// straight into registers touch sixteen half-used 128-byte lines per
-// instruction and left the streaming kernel bound by A's loads once M passed
-// 8. Wave w takes the K blocks kb = w (mod 16): per block, one MFMA per 16
-// activation rows (the MFMA's W rows 8..15 repeat rows 0..7, and those
-// outputs are dropped), then the scale FMAs. The sixteen waves' partial sums
-// are added through LDS in wave order: deterministic, one launch, no
-// workspace. Every global load of the kernel is one of these copies, so the
-// kernel alone counts them when it waits. (N = 2048, K = 7168: M = 12 / 16 /
-// 24 / 32 in 7.0 / 7.2 / 9.0 / 9.1 us, against 8.7 / 9.6 / 9.8 / 10.0 us
-// with the streaming kernel or the split-K kernel and its reduce. Past
-// M = 32 every CU would read more of A than of W, and the split-K kernel is
-// faster: 13.3 against 11.0 us at M = 48.)
+// Decode with A staged through LDS (8 < M <= 32, and 32 < M <= 64 when
+// N <= kFull2dMaxN). The output is tiled in two dimensions: a workgroup
+// takes NR W rows over the whole of K against one group of MP = 16 MT
+// activation rows (blockIdx.y), with sixteen waves. A, W and both scales
+// reach it through the per-CU copy path in that path's efficient form: 1 KiB
+// copies (eight rows of 128 bytes, buffer loads with the LDS bit) of chunks
+// of CB K blocks, two chunks in flight. Fragment loads straight into
+// registers touch sixteen half-used 128-byte lines per instruction and left
+// the streaming kernel bound by A's loads once M passed 8. Wave w takes the
+// K blocks kb = w (mod 16): per block, one MFMA per 16 activation rows, then
+// the scale FMAs. The sixteen waves' partial sums are added through LDS in
+// wave order: deterministic, one launch, no workspace. Every global load of
+// the kernel is one of these copies, so the kernel alone counts them when it
+// waits.
+//
+// Every CU reads its W rows and its group's activation rows over all of K,
+// so the shape of the tile sets the bytes per CU: 8 W rows (the MFMA's rows
+// 8..15 repeat rows 0..7, and those outputs are dropped) against all M <= 16
+// rows; 16 W rows against two groups of 16 rows for 16 < M <= 32 (32 rows
+// per CU instead of 8 + 32); 16 W rows against two groups of 32 rows for
+// 32 < M <= 64 (48 rows per CU instead of 8 + 64). The grid is N / 8 in
+// every case; the two groups' workgroups of one W tile have ids 2048 / 16 =
+// 128 apart, a multiple of 8, so they run on one XCD and the second read of
+// their W rows comes from its L2. Decode shape (N = 2048, K = 7168,
+// graph-replayed, rotated inputs): M = 12 / 16 / 24 / 32 in 7.0 / 7.2 /
+// 8.2 / 8.2 us, and M = 33 / 48 / 64 in 9.8 / 9.9 / 10.1 us in one launch
+// (the split-K kernel and its reduce: 10.6 / 11.0 / 11.9 us). Past
+// N = 2048 the grid no longer fits one round of the CUs, and the split-K
+// kernel is faster (M = 64, N = 4096: 17.7 against 18.9 us).
 // ---------------------------------------------------------------------------
-constexpr int kFullMaxM = 32;
 constexpr int kFullWaves = 16;
-constexpr int kFullRows = 8;
-template <int MT>
+// MT: 16-row tiles of A per workgroup (MP = 16 MT rows, one M group);
+// NR: W rows per workgroup (8: the MFMA's rows 8..15 repeat rows 0..7; 16)
+template <int MT, int NR>
 struct FullCfg {
-  static constexpr int MP = 16 * MT;                    // A rows staged (M rounded up to 16)
-  static_assert(MT == 1 || MT == 2, "M <= 32");
-  static constexpr int CB = MT == 1 ? 16 : 8;           // K blocks per chunk
+  static constexpr int MP = 16 * MT;                    // A rows staged per M group
+  static_assert(MT == 1 || MT == 2, "one or two 16-row tiles");
+  static_assert(NR == 8 || NR == 16, "8 or 16 W rows");
+  static constexpr int CB = MT == 1 && NR == 8 ? 16 : 8;   // K blocks per chunk
   static constexpr int NBUF = 3;                        // chunk buffers (two chunks in flight)
   static constexpr int kAChunk = MP * CB * 128;         // A bytes per chunk
-  static constexpr int kWChunk = kFullRows * CB * 128;  // W bytes per chunk
+  static constexpr int kWChunk = NR * CB * 128;         // W bytes per chunk
   static constexpr int kSChunk = (MP * CB * 4 + 1023) / 1024 * 1024;   // activation scales per chunk (padded to 1 KiB)
   static constexpr int kChunk = kAChunk + kWChunk + kSChunk + 256;   // + the weight scales
   static constexpr int kSCopies4 = MP * CB * 4 / 256;        // 256-byte scale copies per chunk
@@ -1210,46 +1230,29 @@ struct FullCfg {
   static_assert(NBUF * kChunk <= 160 * 1024, "LDS");
 };
 
-// SC16: the activation scales go in one 1 KiB copy per chunk (rows of K/128
-// floats 16-byte aligned: K/128 a multiple of 4), else in 256-byte copies
-template <int MT, bool TS, bool SC16>
+template <int MT, int NR, bool TS, bool SC16>
 __global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, uint16_t* __restrict__ C, int M, int64_t N, int64_t K) {
-  using F = FullCfg<MT>;
+  using F = FullCfg<MT, NR>;
   constexpr int MP = F::MP, CB = F::CB;
-  // NBUF chunk buffers, each [A: CB blocks x MP rows x 128][W: CB blocks x 8
-  // rows x 128][activation scales: MP x CB][weight scales: CB]
   __shared__ __attribute__((aligned(1024))) uint8_t lds[F::NBUF * F::kChunk];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kFullRows;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * NR;
+  const int m0 = static_cast<int>(blockIdx.y) * MP;      // first A row of this M group
+  const int Mg = min(M - m0, MP);                         // its rows
   const int KB = static_cast<int>(K / kBK);
   const int nchunks = (KB + CB - 1) / CB;
   const uint32_t lds0 = lds_addr(lds);
 
-  // Copies of chunk c: kTot copies, copy k issued by wave k % 16 (no copy is
-  // issued twice: each copy instruction costs the copy path about the same
-  // whatever its size, and repeating the small scale copies in every wave
-  // cost 2-3 us per call at M = 64):
-  // - A copy k < kACopies covers K block k / (MP/8) of the chunk and rows
-  //   8 (k % (MP/8)) .. +7; lane l fetches row r = 8 (k % (MP/8)) + l/8, the
-  //   16-byte piece that the row swizzle puts at LDS position l % 8. Rows at
-  //   or past M read zeros (range-checked buffer).
-  // - W copy: block cb of the chunk, the workgroup's 8 rows.
-  // - activation-scale copies: the chunk's [row][CB] floats, in one 1 KiB
-  //   copy (4 floats a lane) when the rows are 16-byte aligned, else in
-  //   256-byte copies of 64 floats.
-  // - weight-scale copy: the chunk's CB weight scales (the workgroup's 8 rows
-  //   sit in one 128-row block; lanes past CB fetch floats never used).
-  // Blocks past K/128 in the last chunk read the next row or zeros and are
-  // never used.
   constexpr int kACopies = MP * CB / 8;
+  constexpr int kWCopies = NR * CB / 8;
   constexpr int kSCopies = SC16 ? 1 : F::kSCopies4;
-  constexpr int kTot = kACopies + CB + (TS ? 0 : kSCopies + 1);
-  const v4i_rsrc ar = make_rsrc(A, static_cast<uint32_t>(M * K));
-  const v4i_rsrc wr = make_rsrc(W + n0 * K, static_cast<uint32_t>(kFullRows * K));
-  const v4i_rsrc sr = make_rsrc(sa, static_cast<uint32_t>(M * KB * 4));
+  constexpr int kTot = kACopies + kWCopies + (TS ? 0 : kSCopies + 1);
+  const v4i_rsrc ar = make_rsrc(A + static_cast<int64_t>(m0) * K, static_cast<uint32_t>(Mg * K));
+  const v4i_rsrc wr = make_rsrc(W + n0 * K, static_cast<uint32_t>(NR * K));
+  const v4i_rsrc sr = make_rsrc(sa + static_cast<int64_t>(m0) * KB, static_cast<uint32_t>(Mg * KB * 4));
   const v4i_rsrc swr = make_rsrc(sw + (n0 / 128) * KB, static_cast<uint32_t>(KB * 4));
   auto issue_chunk = [&](int c) {
     const uint32_t base = lds0 + (c % F::NBUF) * F::kChunk;
@@ -1260,18 +1263,19 @@ __global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_
         const uint32_t off = static_cast<uint32_t>(r * K) + static_cast<uint32_t>(c * CB + cb) * kBK +
                              static_cast<uint32_t>(((lane & 7) ^ swz(r)) << 4);
         copy16_buf_to_lds(off, ar, base + k * 1024);
-      } else if (k < kACopies + CB) {
-        const int cb = k - kACopies;
-        const int r = lane >> 3;
+      } else if (k < kACopies + kWCopies) {
+        const int idx = k - kACopies;
+        const int cb = idx / (NR / 8);
+        const int r = 8 * (idx % (NR / 8)) + (lane >> 3);
         const uint32_t off = static_cast<uint32_t>(r * K) + static_cast<uint32_t>(c * CB + cb) * kBK +
                              static_cast<uint32_t>(((lane & 7) ^ swz(r)) << 4);
-        copy16_buf_to_lds(off, wr, base + F::kAChunk + cb * 1024);
-      } else if (k < kACopies + CB + kSCopies) {
+        copy16_buf_to_lds(off, wr, base + F::kAChunk + idx * 1024);
+      } else if (k < kACopies + kWCopies + kSCopies) {
         if constexpr (SC16) {
           const int r = (4 * lane) / CB, x = (4 * lane) % CB;
           copy16_buf_to_lds(static_cast<uint32_t>((r * KB + c * CB + x) * 4), sr, base + F::kAChunk + F::kWChunk);
         } else {
-          const int s = k - kACopies - CB;
+          const int s = k - kACopies - kWCopies;
           const int e = s * 64 + lane;
           const int r = e / CB, x = e % CB;
           copy4_buf_to_lds(static_cast<uint32_t>((r * KB + c * CB + x) * 4), sr,
@@ -1283,9 +1287,8 @@ __global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_
       }
     }
   };
-  // this wave's copies per chunk: the first kTot % 16 waves issue one more
   constexpr int kFew = kTot / kFullWaves, kExtra = kTot % kFullWaves;
-  auto wait_chunks = [&](auto n) {   // all but this wave's copies of the last n chunks issued are done
+  auto wait_chunks = [&](auto n) {
     constexpr int kN = decltype(n)::value;
     if (wave < kExtra)
       wait_vmcnt<kN * (kFew + 1)>();
@@ -1295,9 +1298,6 @@ __global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_
 
   const float tscale = TS ? sa[0] * sw[0] : 0.0f;
 
-  // chunks 0 .. NBUF-2 now; chunk c + NBUF - 1 right after the barrier that
-  // opens chunk c (every wave is then done with chunk c-1, whose buffer it
-  // refills), so NBUF - 1 chunks stay in flight behind the one computed
   for (int c = 0; c < F::NBUF - 1; ++c)
     if (c < nchunks) issue_chunk(c);
 
@@ -1306,8 +1306,6 @@ __global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_
   for (int j = 0; j < MT; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const int c0 = 2 * (lane >> 4);
   for (int c = 0; c < nchunks; ++c) {
-    // chunk c's copies are done once at most those of the chunks issued
-    // after it remain: min(NBUF - 2, nchunks - 1 - c) chunks
     const int after = min(F::NBUF - 2, nchunks - 1 - c);
     if (after >= 2)
       wait_chunks(std::integral_constant<int, 2>{});
@@ -1315,17 +1313,17 @@ __global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_
       wait_chunks(std::integral_constant<int, 1>{});
     else
       wait_vmcnt<0>();
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of chunk c-1 are back
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
     if (c + F::NBUF - 1 < nchunks) issue_chunk(c + F::NBUF - 1);
     const uint8_t* chunk = lds + (c % F::NBUF) * F::kChunk;
     const float* ss = reinterpret_cast<const float*>(chunk + F::kAChunk + F::kWChunk);
-    const float* sws = ss + MP * CB;
+    const float* sws = ss + F::kSChunk / 4;   // the weight scales follow the padded activation scales
     for (int x = (wave - c * CB) & 15; x < CB; x += 16) {
       const int kb = c * CB + x;
       if (kb >= KB) break;
       const float swb = TS ? 1.0f : sws[x];
-      const v8i wf = lds_frag(chunk + F::kAChunk + x * 1024, lane & 7, c0);
+      const v8i wf = lds_frag(chunk + F::kAChunk + x * NR * 128, lane & (NR - 1), c0);
 #pragma unroll
       for (int j = 0; j < MT; ++j) {
         const v8i af = lds_frag(chunk + x * MP * 128, j * 16 + (lane & 15), c0);
@@ -1336,22 +1334,21 @@ __global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_
       }
     }
   }
-  // every wave is done with the chunk buffers (and no copy is in flight: the
-  // last chunk waited for all of them)
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __syncthreads();
 
-  // the waves' partial sums, [wave][j][lane] float4, over the chunk buffers
   float4* red = reinterpret_cast<float4*>(lds);
 #pragma unroll
   for (int j = 0; j < MT; ++j)
     red[(wave * MT + j) * 64 + lane] = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
   __syncthreads();
-  // thread t < 2M: activation row m = t/2, W rows n0 + 4 (t%2) .. +3, which
-  // lane 16 (t%2) + m%16 of tile m/16 holds in every wave; added in wave order
+  // thread t < (NR/4) Mg: activation row m = t / (NR/4) of the group, W rows
+  // n0 + 4 q .. +3 (q = t % (NR/4)), which lane 16 q + m%16 of tile m/16
+  // holds in every wave; added in wave order
+  constexpr int Q = NR / 4;
   const int t = static_cast<int>(threadIdx.x);
-  if (t < 2 * M) {
-    const int m = t >> 1, q = t & 1;
+  if (t < Q * Mg) {
+    const int m = t / Q, q = t % Q;
     const int l = 16 * q + (m & 15), j = m >> 4;
     float4 s = red[j * 64 + l];
     for (int w = 1; w < kFullWaves; ++w) {
@@ -1361,27 +1358,32 @@ __global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_
     uint2 o;
     o.x = bf16x2_rne(s.x, s.y);
     o.y = bf16x2_rne(s.z, s.w);
-    *reinterpret_cast<uint2*>(C + static_cast<int64_t>(m) * N + n0 + 4 * q) = o;
+    *reinterpret_cast<uint2*>(C + static_cast<int64_t>(m0 + m) * N + n0 + 4 * q) = o;
   }
 }
 
 template <bool TS>
 int launch_decode_full(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c,
                        int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(N / kFullRows));
   const int m = static_cast<int>(M);
   const bool sc16 = TS || (K / kBK) % 4 == 0;
-#define FP8BS_FULL(MT)                                                                                     \
-  if (sc16)                                                                                                 \
-    hipLaunchKernelGGL((gemm_blockscaled_decode_full_kernel<MT, TS, true>), grid, dim3(64 * kFullWaves), 0, st, \
-                       a, sa, w, sw, c, m, N, K);                                                           \
-  else                                                                                                      \
-    hipLaunchKernelGGL((gemm_blockscaled_decode_full_kernel<MT, TS, false>), grid, dim3(64 * kFullWaves), 0, st, \
-                       a, sa, w, sw, c, m, N, K)
+#define FP8BS_FULL(MT, NR, MG)                                                                              \
+  do {                                                                                                      \
+    const dim3 grid(static_cast<unsigned>(N / NR), MG);                                                     \
+    if (sc16)                                                                                               \
+      hipLaunchKernelGGL((gemm_blockscaled_decode_full_kernel<MT, NR, TS, true>), grid, dim3(64 * kFullWaves), \
+                         0, st, a, sa, w, sw, c, m, N, K);                                                  \
+    else                                                                                                    \
+      hipLaunchKernelGGL((gemm_blockscaled_decode_full_kernel<MT, NR, TS, false>), grid, dim3(64 * kFullWaves), \
+                         0, st, a, sa, w, sw, c, m, N, K);                                                  \
+  } while (0)
+  // N / 8 workgroups in each case
   if (m <= 16) {
-    FP8BS_FULL(1);
+    FP8BS_FULL(1, 8, 1);
+  } else if (m <= 32) {
+    FP8BS_FULL(1, 16, 2);
   } else {
-    FP8BS_FULL(2);
+    FP8BS_FULL(2, 16, 2);
   }
 #undef FP8BS_FULL
   return FP8BS_OK;
@@ -1432,7 +1434,7 @@ inline bool gemm_shape_ok(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0) return false;
   if (M > (INT64_MAX / K) || M > (INT64_MAX / N) || N > (INT64_MAX / K)) return false;
   if (K > (int64_t{1} << 22) || (M + 127) / 128 > 0x7FFFFFFF) return false;
-  if (use_decode(M) && M > kFullMaxM && K / 128 > static_cast<int64_t>(kDecMaxSplits) * kDecMaxKb)
+  if (use_split_k(M, N) && K / 128 > static_cast<int64_t>(kDecMaxSplits) * kDecMaxKb)
     return false;
   return true;
 }
@@ -1446,7 +1448,7 @@ extern "C" {
 
 size_t fp8_gemm_blockscaled_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (!gemm_shape_ok(M, N, K)) return 0;
-  return use_decode(M) && M > kFullMaxM ? decode_workspace_bytes(M, N, K) : 0;
+  return use_split_k(M, N) ? decode_workspace_bytes(M, N, K) : 0;
 }
 
 }  // extern "C"
@@ -1477,7 +1479,7 @@ int gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m
   if (use_decode(M)) {
     if (M <= kDecStreamMaxM)
       rc = launch_decode_stream<MODE == 2>(a, a_scale, w, w_scale, c, M, N, K, st);
-    else if (M <= kFullMaxM)
+    else if (!use_split_k(M, N))
       rc = launch_decode_full<MODE == 2>(a, a_scale, w, w_scale, c, M, N, K, st);
     else
       rc = launch_decode<MODE == 2>(a, a_scale, w, w_scale, c, static_cast<float*>(workspace), M, N, K, st);

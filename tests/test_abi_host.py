@@ -154,18 +154,21 @@ def test_python_binding_rejects_bad_tensors():
 def test_gemm_k_limits(L):
     # copy offsets within a tile are 32-bit: K above 2^22 is rejected
     assert L.fp8_gemm_blockscaled(P, P, P, P, P, 8, 128, (1 << 22) + 128, None, 0, None) == ESHAPE
-    # 32 < M <= 64 splits K into at most 32 parts of at most 16 blocks; M <= 32
-    # takes all of K in one workgroup and has no such limit
-    assert L.fp8_gemm_blockscaled(P, P, P, P, P, 33, 128, 128 * 513, None, 0, None) == ESHAPE
+    # 32 < M <= 64 with N > 2048 splits K into at most 32 parts of at most 16
+    # blocks; M <= 32, and M <= 64 with N <= 2048, take all of K in one
+    # workgroup and have no such limit
+    assert L.fp8_gemm_blockscaled(P, P, P, P, P, 33, 2176, 128 * 513, None, 0, None) == ESHAPE
     assert L.fp8_gemm_blockscaled_workspace_bytes(32, 128, 128 * 513) == 0
-    for M in (1, 8, 9, 16, 17, 32):
+    assert L.fp8_gemm_blockscaled_workspace_bytes(64, 2048, 128 * 513) == 0
+    for M in (1, 8, 9, 16, 17, 32, 33, 48, 64):
         assert L.fp8_gemm_blockscaled_workspace_bytes(M, 2048, 7168) == 0
-    assert L.fp8_gemm_blockscaled_workspace_bytes(33, 2048, 7168) > 0
+    assert L.fp8_gemm_blockscaled_workspace_bytes(33, 2176, 7168) > 0
+    assert L.fp8_gemm_blockscaled_workspace_bytes(64, 4096, 7168) > 0
     # a shape the call rejects needs no workspace, and the act-quant + GEMM
     # call rejects it before enqueuing anything
-    assert L.fp8_gemm_blockscaled_workspace_bytes(40, 128, 128 * 513) == 0
-    assert L.fp8_act_quant_gemm_blockscaled_workspace_bytes(40, 128, 128 * 513) == 0
-    assert L.fp8_act_quant_gemm_blockscaled(P, P, P, P, 40, 128, 128 * 513, P, 1 << 30, None) == ESHAPE
+    assert L.fp8_gemm_blockscaled_workspace_bytes(40, 2176, 128 * 513) == 0
+    assert L.fp8_act_quant_gemm_blockscaled_workspace_bytes(40, 2176, 128 * 513) == 0
+    assert L.fp8_act_quant_gemm_blockscaled(P, P, P, P, 40, 2176, 128 * 513, P, 1 << 30, None) == ESHAPE
 
 
 def test_ue8m0_argument_errors(L):

@@ -33,9 +33,10 @@ def test_act_quant_outputs_checked():
 def test_gemm_out_and_workspace_checked():
     fb = binding()
     say("binding: GEMM out= and workspace checks")
-    d = synth.gen_c3(48)      # the split-K decode path: a workspace is needed
-    qa, sa = quant.act_quant_block(d["a"])
-    qw, sw = quant.weight_quant_block(d["w"])
+    # M = 48, N = 2304: the split-K decode path, which needs a workspace
+    rng = np.random.default_rng(48)
+    qa, sa = quant.act_quant_block(synth.f64_to_bf16_bits(rng.standard_normal((48, 1024)) * 3))
+    qw, sw = quant.weight_quant_block(synth.f64_to_bf16_bits(rng.standard_normal((2304, 1024)) * 0.02))
     args = (u8_to_dev(qa), f32_to_dev(sa), u8_to_dev(qw), f32_to_dev(sw))
     M, N = qa.shape[0], qw.shape[0]
     with pytest.raises(ValueError):

@@ -250,6 +250,8 @@ def test_bit_exact_against_matrix_core_model_large_tiles(dist):
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (5, 256, 1024), (16, 2048, 7168), (17, 384, 2048),
                                    (33, 640, 4096), (64, 2048, 7168), (64, 128, 128 * 40), (48, 7168, 2048),
+                                   (33, 2048, 7168), (48, 2048, 7168), (37, 1152, 128 * 13), (56, 2048, 128),
+                                   (64, 256, 128 * 513), (33, 2176, 1280), (64, 4096, 7168), (40, 2304, 128 * 9),
                                    (3, 256, 128 * 7), (16, 128, 128 * 600), (40, 128, 128 * 500),
                                    (2, 128, 71424), (2, 128, 71552), (13, 384, 128 * 9), (9, 128, 128),
                                    (24, 2048, 7168), (32, 2048, 7168), (20, 256, 128 * 5), (31, 384, 128 * 37),
@@ -260,14 +262,17 @@ def test_decode_shapes(M, N, K):
     # without a step; K = 600 blocks runs many prefetch rounds per wave); two
     # K blocks packed into each MFMA (8 W rows per workgroup): an odd block
     # count (1, 7, 559) leaves the last step half empty.
-    # 8 < M <= 32: 8 W rows per workgroup over all of K, A streamed through
-    # LDS in chunks of 16 (M <= 16) or 8 K blocks, three chunk buffers: one
-    # block (K = 128), a partial chunk (5, 9, 17, 37 blocks), activation-scale
-    # rows that are not 16-byte aligned (K/128 = 5, 9, 17, 37, 513: 256-byte
-    # scale copies) and aligned ones (56, 1000: one 1 KiB copy), many chunks
-    # (1000 and 513 blocks, past the split-K kernel's limit).
-    # 32 < M <= 64: several K splits, fp32 partials in the workspace, reduced
-    # in split order.
+    # 8 < M <= 32, and 32 < M <= 64 with N <= 2048: W rows and one group of
+    # activation rows per workgroup over all of K (8 W rows against all
+    # M <= 16 rows; 16 W rows against groups of 16 or 32 rows, the second
+    # group partial when M is not 32 or 64), A streamed through LDS in chunks
+    # of 16 or 8 K blocks, three chunk buffers: one block (K = 128), a
+    # partial chunk (5, 9, 13, 17, 37 blocks), activation-scale rows that are
+    # not 16-byte aligned (K/128 = 5, 9, 13, 17, 37, 513: 256-byte scale
+    # copies) and aligned ones (56, 1000: one 1 KiB copy), many chunks (1000
+    # and 513 blocks, past the split-K kernel's limit).
+    # 32 < M <= 64 with N > 2048: several K splits, fp32 partials in the
+    # workspace, reduced in split order.
     rng = np.random.default_rng(M * 7 + N + K)
     a = synth.f64_to_bf16_bits(rng.standard_normal((M, K)) * 3)
     w = synth.f64_to_bf16_bits(rng.standard_normal((N, K)) * 0.02)
@@ -276,14 +281,15 @@ def test_decode_shapes(M, N, K):
 
 def test_gemm_workspace_size_and_reuse():
     fb = binding()
-    N, K = 2048, 7168
-    for M in (1, 8, 16, 32, 65, 4096):
-        assert fb.fp8_gemm_blockscaled_workspace_bytes(M, N, K) == 0
-    M = 48
+    for M in (1, 8, 16, 32, 33, 64, 65, 4096):
+        assert fb.fp8_gemm_blockscaled_workspace_bytes(M, 2048, 7168) == 0
+    # the split-K kernel (32 < M <= 64, N > 2048)
+    M, N, K = 48, 4096, 2048
     wsb = fb.fp8_gemm_blockscaled_workspace_bytes(M, N, K)
     assert wsb >= M * N * 4 and wsb % (M * N * 4) == 0    # fp32 partials, one [M, N] per K split
-    d = synth.gen_c3(M)
-    qa, sa, qw, sw = operands(d["a"], d["w"])
+    rng = np.random.default_rng(4096)
+    qa, sa, qw, sw = operands(synth.f64_to_bf16_bits(rng.standard_normal((M, K)) * 3),
+                              synth.f64_to_bf16_bits(rng.standard_normal((N, K)) * 0.02))
     args = (u8_to_dev(qa), f32_to_dev(sa), u8_to_dev(qw), f32_to_dev(sw))
     ws = torch.full((wsb,), 0x7F, dtype=torch.uint8, device="cuda:0")     # garbage on entry
     c1 = fb.fp8_gemm_blockscaled(*args, workspace=ws)
@@ -293,12 +299,12 @@ def test_gemm_workspace_size_and_reuse():
     c3 = fb.fp8_gemm_blockscaled(*args, workspace=ws_seq)
     torch.cuda.synchronize()
     assert torch.equal(c1, c2) and torch.equal(c1, c3)
-    check_full(qa, sa, qw, sw, "decode M=48 through a reused workspace", c=to_bf16_bits(c2))
+    check_full(qa, sa, qw, sw, "decode 48x4096x2048 through a reused workspace", c=to_bf16_bits(c2))
     with pytest.raises(fb.Fp8bsError):
         fb.fp8_gemm_blockscaled(*args, workspace=ws[: wsb - 4])
 
 
-@pytest.mark.parametrize("M", [1, 5, 8, 12, 16, 24, 32, 40])
+@pytest.mark.parametrize("M", [1, 5, 8, 12, 16, 24, 32, 40, 64])
 def test_decode_paths_are_deterministic(M):
     # the decode kernels add their partial sums in a fixed order (waves, K
     # block groups, K splits), so repeated calls give identical bits

@@ -90,17 +90,18 @@ def gemm_inputs(fb, M, N, K, r, quant=None):
     return [qa, sa, qw, sw]
 
 
-# decode M = 1 (packed K blocks), 12 (16 rows per workgroup), 40 and 64
-# (split-K with the reduce kernel); M = 300 and 2048 (tiled kernel)
+# decode M = 1 (packed K blocks), 12, 40 and 64 at N = 2048 (chunked full-K
+# kernel), 40 and 64 at N = 4096 (split-K with the reduce kernel); M = 300
+# and 2048 (tiled kernel)
 @pytest.mark.parametrize("M,N,K", [(1, 2048, 7168), (12, 2048, 7168), (40, 2048, 7168), (64, 2048, 7168),
-                                   (300, 1024, 2048), (2048, 2048, 2048)])
+                                   (40, 4096, 2048), (64, 4096, 7168), (300, 1024, 2048), (2048, 2048, 2048)])
 def test_gemm_blockscaled(M, N, K):
     fb = binding()
     replay_matches_eager(f"gemm_blockscaled {M}x{N}x{K}", lambda r: gemm_inputs(fb, M, N, K, r),
                          fb.fp8_gemm_blockscaled)
 
 
-@pytest.mark.parametrize("M,N,K", [(40, 2048, 7168), (2048, 2048, 2048)])
+@pytest.mark.parametrize("M,N,K", [(40, 2048, 7168), (40, 4096, 2048), (2048, 2048, 2048)])
 def test_gemm_ue8m0(M, N, K):
     fb = binding()
 
@@ -112,7 +113,7 @@ def test_gemm_ue8m0(M, N, K):
     replay_matches_eager(f"gemm_ue8m0 {M}x{N}x{K}", inputs, fb.fp8_gemm_blockscaled_ue8m0)
 
 
-@pytest.mark.parametrize("M,N,K", [(40, 2048, 7168), (2048, 2048, 2048)])
+@pytest.mark.parametrize("M,N,K", [(40, 2048, 7168), (40, 4096, 2048), (2048, 2048, 2048)])
 def test_gemm_tensorscaled(M, N, K):
     fb = binding()
 
@@ -124,12 +125,12 @@ def test_gemm_tensorscaled(M, N, K):
     replay_matches_eager(f"gemm_tensorscaled {M}x{N}x{K}", inputs, fb.fp8_gemm_tensorscaled)
 
 
-# M = 2: one kernel; M = 8: act-quant and GEMM through the workspace;
-# M = 48: act-quant, split-K GEMM and its reduce
-@pytest.mark.parametrize("M", [2, 8, 48])
-def test_act_quant_gemm(M):
+# M = 2: one kernel; M = 8 and 48 at N = 2048: act-quant and GEMM through the
+# workspace; M = 48 at N = 4096: act-quant, split-K GEMM and its reduce
+@pytest.mark.parametrize("M,N", [(2, 2048), (8, 2048), (48, 2048), (48, 4096)])
+def test_act_quant_gemm(M, N):
     fb = binding()
-    N, K = 2048, 7168
+    K = 7168
 
     def inputs(r):
         qw, sw = fb.fp8_weight_quant_block(bf16((N, K), 1000 + r, 0.02))
