@@ -1185,11 +1185,11 @@ int launch_decode(const uint8_t* a, const float* sa, const uint8_t* w, const flo
 // activation rows (blockIdx.y), with sixteen waves. A, W and both scales
 // reach it through the per-CU copy path in that path's efficient form: 1 KiB
 // copies (eight rows of 128 bytes, buffer loads with the LDS bit) of chunks
-// of CB K blocks, two chunks in flight. Fragment loads straight into
-// registers touch sixteen half-used 128-byte lines per instruction and left
-// the streaming kernel bound by A's loads once M passed 8. Wave w takes the
-// K blocks kb = w (mod 16): per block, one MFMA per 16 activation rows, then
-// the scale FMAs. The sixteen waves' partial sums are added through LDS in
+// of CB K blocks, two chunks in flight (three with 16 x 16 tiles). Fragment
+// loads straight into registers touch sixteen half-used 128-byte lines per
+// instruction and left the streaming kernel bound by A's loads once M passed
+// 8. Wave w takes the K blocks kb = w (mod 16): per block, one MFMA per 16
+// activation rows, then the scale FMAs. The sixteen waves' partial sums are added through LDS in
 // wave order: deterministic, one launch, no workspace. Every global load of
 // the kernel is one of these copies, so the kernel alone counts them when it
 // waits.
@@ -1218,7 +1218,10 @@ struct FullCfg {
   static_assert(MT == 1 || MT == 2, "one or two 16-row tiles");
   static_assert(NR == 8 || NR == 16, "8 or 16 W rows");
   static constexpr int CB = MT == 1 && NR == 8 ? 16 : 8;   // K blocks per chunk
-  static constexpr int NBUF = 3;                        // chunk buffers (two chunks in flight)
+  // chunk buffers: three (two chunks in flight), four where they fit (16 W
+  // rows against 16 activation rows: 8.0 against 8.2 us at M = 24; chunks of
+  // 4 K blocks with five or six buffers were 15-30% slower everywhere)
+  static constexpr int NBUF = MT == 1 && NR == 16 ? 4 : 3;
   static constexpr int kAChunk = MP * CB * 128;         // A bytes per chunk
   static constexpr int kWChunk = NR * CB * 128;         // W bytes per chunk
   static constexpr int kSChunk = (MP * CB * 4 + 1023) / 1024 * 1024;   // activation scales per chunk (padded to 1 KiB)
