@@ -1189,10 +1189,10 @@ int launch_decode(const uint8_t* a, const float* sa, const uint8_t* w, const flo
 // loads straight into registers touch sixteen half-used 128-byte lines per
 // instruction and left the streaming kernel bound by A's loads once M passed
 // 8. Wave w takes the K blocks kb = w (mod 16): per block, one MFMA per 16
-// activation rows, then the scale FMAs. The sixteen waves' partial sums are added through LDS in
-// wave order: deterministic, one launch, no workspace. Every global load of
-// the kernel is one of these copies, so the kernel alone counts them when it
-// waits.
+// activation rows, then the scale FMAs. The sixteen waves' partial sums are
+// added through LDS in wave order: deterministic, one launch, no workspace.
+// Every global load of the kernel is one of these copies, so the kernel
+// alone counts them when it waits.
 //
 // Every CU reads its W rows and its group's activation rows over all of K,
 // so the shape of the tile sets the bytes per CU: 8 W rows (the MFMA's rows
@@ -1233,12 +1233,16 @@ struct FullCfg {
   static_assert(NBUF * kChunk <= 160 * 1024, "LDS");
 };
 
+// SC16: the activation scales go in one 1 KiB copy per chunk (rows of K/128
+// floats 16-byte aligned: K/128 a multiple of 4), else in 256-byte copies
 template <int MT, int NR, bool TS, bool SC16>
 __global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, uint16_t* __restrict__ C, int M, int64_t N, int64_t K) {
   using F = FullCfg<MT, NR>;
   constexpr int MP = F::MP, CB = F::CB;
+  // NBUF chunk buffers, each [A: CB blocks x MP rows x 128][W: CB blocks x NR
+  // rows x 128][activation scales: MP x CB, padded to 1 KiB][weight scales: CB]
   __shared__ __attribute__((aligned(1024))) uint8_t lds[F::NBUF * F::kChunk];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1249,6 +1253,24 @@ __global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_
   const int nchunks = (KB + CB - 1) / CB;
   const uint32_t lds0 = lds_addr(lds);
 
+  // Copies of chunk c: kTot copies, copy k issued by wave k % 16 (no copy is
+  // issued twice: each copy instruction costs the copy path about the same
+  // whatever its size, and repeating the small scale copies in every wave
+  // cost 2-3 us per call at M = 64):
+  // - A copy k < kACopies covers K block k / (MP/8) of the chunk and the
+  //   group's rows 8 (k % (MP/8)) .. +7; lane l fetches row r = 8 (k % (MP/8))
+  //   + l/8, the 16-byte piece that the row swizzle puts at LDS position
+  //   l % 8. Rows at or past the group's last read zeros (range-checked
+  //   buffer).
+  // - W copies: NR/8 per K block of the chunk, eight of the workgroup's rows
+  //   each, laid out like A.
+  // - activation-scale copies: the chunk's [row][CB] floats, in one 1 KiB
+  //   copy (4 floats a lane) when the rows are 16-byte aligned, else in
+  //   256-byte copies of 64 floats.
+  // - weight-scale copy: the chunk's CB weight scales (the workgroup's NR
+  //   rows sit in one 128-row block; lanes past CB fetch floats never used).
+  // Blocks past K/128 in the last chunk read the next row or zeros and are
+  // never used.
   constexpr int kACopies = MP * CB / 8;
   constexpr int kWCopies = NR * CB / 8;
   constexpr int kSCopies = SC16 ? 1 : F::kSCopies4;
@@ -1290,8 +1312,9 @@ __global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_
       }
     }
   };
+  // this wave's copies per chunk: the first kTot % 16 waves issue one more
   constexpr int kFew = kTot / kFullWaves, kExtra = kTot % kFullWaves;
-  auto wait_chunks = [&](auto n) {
+  auto wait_chunks = [&](auto n) {   // all but this wave's copies of the last n chunks issued are done
     constexpr int kN = decltype(n)::value;
     if (wave < kExtra)
       wait_vmcnt<kN * (kFew + 1)>();
@@ -1301,6 +1324,9 @@ __global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_
 
   const float tscale = TS ? sa[0] * sw[0] : 0.0f;
 
+  // chunks 0 .. NBUF-2 now; chunk c + NBUF - 1 right after the barrier that
+  // opens chunk c (every wave is then done with chunk c-1, whose buffer it
+  // refills), so NBUF - 1 chunks stay in flight behind the one computed
   for (int c = 0; c < F::NBUF - 1; ++c)
     if (c < nchunks) issue_chunk(c);
 
@@ -1309,6 +1335,8 @@ __global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_
   for (int j = 0; j < MT; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const int c0 = 2 * (lane >> 4);
   for (int c = 0; c < nchunks; ++c) {
+    // chunk c's copies are done once at most those of the chunks issued
+    // after it remain: min(NBUF - 2, nchunks - 1 - c) chunks
     const int after = min(F::NBUF - 2, nchunks - 1 - c);
     if (after >= 2)
       wait_chunks(std::integral_constant<int, 2>{});
@@ -1316,7 +1344,7 @@ __global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_
       wait_chunks(std::integral_constant<int, 1>{});
     else
       wait_vmcnt<0>();
-    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of chunk c-1 are back
     __builtin_amdgcn_s_barrier();
     if (c + F::NBUF - 1 < nchunks) issue_chunk(c + F::NBUF - 1);
     const uint8_t* chunk = lds + (c % F::NBUF) * F::kChunk;
@@ -1337,9 +1365,12 @@ __global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_
       }
     }
   }
+  // every wave is done with the chunk buffers (and no copy is in flight: the
+  // last chunk waited for all of them)
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __syncthreads();
 
+  // the waves' partial sums, [wave][j][lane] float4, over the chunk buffers
   float4* red = reinterpret_cast<float4*>(lds);
 #pragma unroll
   for (int j = 0; j < MT; ++j)
