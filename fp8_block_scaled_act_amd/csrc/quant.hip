@@ -185,13 +185,12 @@ __global__ __launch_bounds__(kThreads) void weight_quant_block_kernel(
 // launches below: 32768 elements 3.9 against 4.9 us, 65536 elements 4.3
 // against 5.0 us; at 98304 elements the workgroup's read of the whole tensor
 // makes it slower, 5.4 against 4.9 us). Large inputs: stage 1 writes one
-// partial max per workgroup to the
-// workspace (grid sized to numel, capped), stage 2 has every workgroup reduce
-// those partials itself before quantizing its share; workgroup 0 writes the
-// scale. No atomics, deterministic. Stage 2 writes the codes with
-// non-temporal stores, which keep them from pushing the input out of the
-// last-level cache before stage 2 has read it (measured: 141 -> 116 us on a
-// 256 MiB tensor, larger than that cache).
+// partial max per workgroup to the workspace (grid sized to numel, capped),
+// stage 2 has every workgroup reduce those partials itself before quantizing
+// its share; workgroup 0 writes the scale. No atomics, deterministic. Stage
+// 2 writes the codes with non-temporal stores, which keep them from pushing
+// the input out of the last-level cache before stage 2 has read it
+// (measured: 141 -> 116 us on a 256 MiB tensor, larger than that cache).
 // ---------------------------------------------------------------------------
 constexpr int64_t kSmallNumel = 1 << 14;
 constexpr int64_t kMidNumel = 1 << 16;
@@ -498,6 +497,8 @@ __global__ __launch_bounds__(kSmallThreads) void tensor_amax_small_kernel(const 
   }
 }
 
+// the amax stage alone for mid-size inputs: one workgroup, eight loads per
+// thread in flight
 __global__ __launch_bounds__(kSmallThreads) void tensor_amax_mid_kernel(const uint16_t* __restrict__ x,
                                                                         int64_t numel, float* __restrict__ amax_out,
                                                                         float* __restrict__ scale) {
