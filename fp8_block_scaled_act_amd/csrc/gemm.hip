@@ -194,12 +194,15 @@ struct TileCfg {
 //         FMAs; the fp32 accumulator is the MFMA's own, chained over K).
 // MODE 2: one scale per tensor (sa[0], sw[0]): products accumulated by the
 //         matrix cores unscaled, the scale product applied in the epilogue.
-template <int BN, int BM, int WN, int WM, int STAGES, int WAVES_PER_EU, int MODE>
+// PART: split K (blockIdx.y = split, kb_per K blocks each) and store the
+// fp32 partial sums [split][M][N] to `part` instead of C; a second kernel adds
+// them in split order.
+template <int BN, int BM, int WN, int WM, int STAGES, int WAVES_PER_EU, int MODE, bool PART = false>
 __global__ __launch_bounds__(64 * WN * WM) __attribute__((amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void gemm_blockscaled_tiled_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, uint16_t* __restrict__ C, int64_t M, int64_t N, int64_t K,
-    int tiles_m, int tiles_n) {
+    int tiles_m, int tiles_n, float* __restrict__ part = nullptr, int kb_per = 0) {
   using T = TileCfg<BN, BM, WN, WM, STAGES>;
   constexpr int NI = T::NI, NJ = T::NJ;
   constexpr bool HW = MODE >= 1;
@@ -226,6 +229,10 @@ void gemm_blockscaled_tiled_kernel(
   const int wn = wave % WN;
   const int wm = wave / WN;
   const int KB = static_cast<int>(K / kBK);
+  // this workgroup's K blocks: [kb0, kb_end) (all of K unless PART)
+  const int sp = PART ? static_cast<int>(blockIdx.y) : 0;
+  const int kb0 = PART ? sp * kb_per : 0;
+  const int kb_end = PART ? min(KB, kb0 + kb_per) : KB;
 
   // --- copy sources: per-lane 32-bit byte offsets into buffers that start
   //     at the tile's first row and end at the matrix's last row (rows past
@@ -292,7 +299,7 @@ void gemm_blockscaled_tiled_kernel(
                         st + T::kWBytes + (wave * T::kALoads + q) * 1024);
     }
     if constexpr (!TS) {
-      if (p == 0 && (kb & (T::kSChunk - 1)) == 0) {
+      if (p == 0 && ((kb & (T::kSChunk - 1)) == 0 || (PART && kb == kb0))) {
         const int c = kb / T::kSChunk;
         const v4i_rsrc sr = make_rsrc(stile + c * T::kSChunk, static_cast<uint32_t>(arows * KB * 4 - c * T::kSChunk * 4));
         const uint32_t sd = lds0 + STAGES * T::kStageBytes + (c & 1) * T::kSChunkBytes + wave * T::kSCopies * 256;
@@ -320,17 +327,17 @@ void gemm_blockscaled_tiled_kernel(
   const int wrow = wn * T::TN + (lane & 15);
   // prologue: block 0's tiles and block 1's A tile (block 1's W tile is
   // copied during block 0)
-  issue(0);
-  if (1 < KB) {
+  issue(kb0);
+  if (kb0 + 1 < kb_end) {
 #pragma unroll
-    for (int q = 0; q < T::kALoads; ++q) issue_part(1, T::kWLoads + q);
+    for (int q = 0; q < T::kALoads; ++q) issue_part(kb0 + 1, T::kWLoads + q);
   }
   constexpr int kPer = T::kWLoads + T::kALoads;   // operand copies per block (scale chunks aside)
   // The weight scale of block kb+1 is loaded (scalar load) after the last
   // fragment read of block kb and waited for right after the next barrier,
   // before the first fragment read: scalar loads complete out of order, so
   // while one is in flight every wait for an LDS read is a full wait.
-  float swb = TS ? 1.0f : swrow[0];
+  float swb = TS ? 1.0f : swrow[kb0];
   // Software pipeline across blocks. The MFMAs of the last W row of block
   // kb-1 are issued after the barrier that opens block kb, interleaved with
   // the reads of block kb's A fragments (each read refills the registers the
@@ -387,7 +394,7 @@ void gemm_blockscaled_tiled_kernel(
     // kb) are done once at most the copies of the blocks issued after it
     // remain: STAGES-2 groups of at least kPer copies while blocks are being
     // prefetched, fewer in the last iterations (loads complete in order)
-    if (kb + 1 < KB)
+    if (kb + 1 < kb_end)
       wait_vmcnt<T::kALoads>();   // block kb+1's A copies, issued last, may be in flight
     else
       wait_vmcnt<0>();
@@ -500,11 +507,11 @@ void gemm_blockscaled_tiled_kernel(
     for (int j = 0; j < NJ; ++j) csl[j] = cs[j];
     }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (!TS) swb = swrow[min(kb + 1, KB - 1)];
+    if constexpr (!TS) swb = swrow[min(kb + 1, kb_end - 1)];
   };
-  const int kb_pf = max(KB - (STAGES - 1), 0);
-  for (int kb = 0; kb < kb_pf; ++kb) step(kb, std::true_type{});
-  for (int kb = kb_pf; kb < KB; ++kb) step(kb, std::false_type{});
+  const int kb_pf = max(kb_end - (STAGES - 1), kb0);
+  for (int kb = kb0; kb < kb_pf; ++kb) step(kb, std::true_type{});
+  for (int kb = kb_pf; kb < kb_end; ++kb) step(kb, std::false_type{});
   if constexpr (HW) {
     // last row of the last block
 #pragma unroll
@@ -539,6 +546,35 @@ void gemm_blockscaled_tiled_kernel(
     for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] *= st;
+  }
+  if constexpr (PART) {
+    // The last MFMA row above must run with every lane active: the stores
+    // below are conditional, and the compiler would otherwise sink those
+    // MFMAs into them, where a scale moved into a VGPR under the partial
+    // EXEC mask leaves stale bytes in the inactive lanes (the matrix cores
+    // read every lane's operands). The empty asm pins the results here.
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(acc[i][j]));
+    // the fp32 partial sums of this K split, 16 bytes a lane (four n of one
+    // m), stored non-temporally: the reduce kernel reads them once
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t m = m0 + wm * T::TM + j * 16 + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int64_t n = n0 + wn * T::TN + i * 16 + (lane >> 4) * 4;
+        if (m < M && n < N) {
+          float* q = part + (static_cast<int64_t>(sp) * M + m) * N + n;
+          __builtin_nontemporal_store(acc[i][j][0], q);
+          __builtin_nontemporal_store(acc[i][j][1], q + 1);
+          __builtin_nontemporal_store(acc[i][j][2], q + 2);
+          __builtin_nontemporal_store(acc[i][j][3], q + 3);
+        }
+      }
+    }
+    return;
   }
   __syncthreads();   // every wave is done reading the last stage
 #pragma unroll
@@ -1461,6 +1497,54 @@ int launch_tiled(const uint8_t* a, const float* sa, const uint8_t* w, const floa
   return FP8BS_OK;
 }
 
+// Split K for the tiled kernel. Past the decode kernels (M > 64), an output
+// with fewer 128 x 128 tiles than CUs leaves most of the chip idle while each
+// workgroup walks all of K (N = 2048, K = 7168: M = 96 to 1024 all took about
+// 48 us, against 10 us at M = 64). K is then split so that about one
+// 128 x 128 workgroup per CU runs (at most kDecMaxSplits splits); each split
+// stores fp32 partial sums and gemm_splitk_reduce_kernel adds them in split
+// order (deterministic) and rounds to bf16. N = 2048, K = 7168: M = 96 / 128
+// / 256 / 512 / 1024 in 16.3 / 16.6 / 19.5 / 26.9 / 38.1 us against 49.6 /
+// 50.7 / 47.5 / 48.9 / 48.8 us; K = 2048: M = 130, N = 384 in 9.2 against
+// 14.4 us, M = 300, N = 1024 in 12.0 against 14.2 us. A short K gains less
+// than the partials and the reduce launch cost once the tiles are many or K
+// is shorter still (M = 128, N = 7168, K = 2048: 17.2 against 17.0 us; M = 96,
+// N = 256, K = 1024 with one scale per tensor: 9.5 against 7.0 us), so K is
+// split from 32 blocks, or from 16 blocks with at most 32 tiles. A target of
+// two workgroups per CU was slower (M = 128: 22.7 us).
+constexpr int64_t kSplitCUs = 256;      // MI355X's CUs: the plan (and the workspace size) is per shape
+struct TiledSplit {
+  int splits;
+  int kb_per;
+};
+inline TiledSplit tiled_split_plan(int64_t M, int64_t N, int64_t K) {
+  const int64_t KB = K / kBK;
+  const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
+  if (use_decode(M) || tiles256 >= kSplitCUs || tiles128 >= kSplitCUs || KB < 16 || (KB < 32 && tiles128 > 32))
+    return {1, static_cast<int>(KB)};
+  int64_t want = (kSplitCUs + tiles128 - 1) / tiles128;
+  want = std::min<int64_t>(std::min<int64_t>(want, KB), kDecMaxSplits);
+  const int kb_per = static_cast<int>((KB + want - 1) / want);
+  return {static_cast<int>((KB + kb_per - 1) / kb_per), kb_per};
+}
+
+template <int MODE>
+int launch_tiled_split(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* c,
+                       float* ws, int64_t M, int64_t N, int64_t K, const TiledSplit& p, hipStream_t st) {
+  const int64_t tiles_m = (M + 127) / 128;
+  const int64_t tiles_n = (N + 127) / 128;
+  const int64_t grid = (tiles_m * tiles_n + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_blockscaled_tiled_kernel<128, 128, 2, 2, 2, 2, MODE, true>),
+                     dim3(static_cast<unsigned>(grid), static_cast<unsigned>(p.splits)), dim3(256), 0, st, a, sa,
+                     w, sw, c, M, N, K, static_cast<int>(tiles_m), static_cast<int>(tiles_n), ws, p.kb_per);
+  if (hipGetLastError() != hipSuccess) return FP8BS_ERR_LAUNCH;
+  const int64_t mn4 = M * N / 4;
+  hipLaunchKernelGGL(gemm_splitk_reduce_kernel, dim3(static_cast<unsigned>((mn4 + 255) / 256)), dim3(256), 0, st,
+                     ws, c, mn4, p.splits);
+  return FP8BS_OK;
+}
+
 // Sizes every GEMM entry point accepts: K and N multiples of 128, products
 // that fit int64, K at most 2^22, and for the split-K decode kernel at most
 // kDecMaxSplits * kDecMaxKb K blocks.
@@ -1482,7 +1566,9 @@ extern "C" {
 
 size_t fp8_gemm_blockscaled_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (!gemm_shape_ok(M, N, K)) return 0;
-  return use_split_k(M, N) ? decode_workspace_bytes(M, N, K) : 0;
+  if (use_split_k(M, N)) return decode_workspace_bytes(M, N, K);
+  const TiledSplit p = tiled_split_plan(M, N, K);
+  return p.splits > 1 ? static_cast<size_t>(p.splits) * M * N * sizeof(float) : 0;
 }
 
 }  // extern "C"
@@ -1500,6 +1586,7 @@ int gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m
     return FP8BS_ERR_ALIGN;
   const size_t need = fp8_gemm_blockscaled_workspace_bytes(M, N, K);
   if (need > 0 && (!workspace || workspace_bytes < need)) return FP8BS_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 16)) return FP8BS_ERR_ALIGN;   // the reduce reads float4
   const DeviceInfo dev = current_device();
   if (dev.status != FP8BS_OK) return dev.status;
   const uint8_t* a = static_cast<const uint8_t*>(a_e4m3);
@@ -1522,9 +1609,13 @@ int gemm_blockscaled(const void* a_e4m3, const float* a_scale, const void* w_e4m
   }
   // 256 x 256 tiles (eight waves, two per SIMD) when they fill the chip,
   // else 128 x 128 tiles (two workgroups per CU)
+  // (K split when even the 128 x 128 tiles are fewer than the CUs)
   const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const TiledSplit sp = tiled_split_plan(M, N, K);
   if (tiles256 >= dev.num_cus)
     rc = launch_tiled<256, 256, 2, 4, 2, 2, MODE>(a, a_scale, w, w_scale, c, M, N, K, st);
+  else if (sp.splits > 1)
+    rc = launch_tiled_split<MODE>(a, a_scale, w, w_scale, c, static_cast<float*>(workspace), M, N, K, sp, st);
   else
     rc = launch_tiled<128, 128, 2, 2, 2, 2, MODE>(a, a_scale, w, w_scale, c, M, N, K, st);
   if (rc != FP8BS_OK) return rc;
@@ -1596,6 +1687,7 @@ int fp8_act_quant_gemm_blockscaled(const void* x_bf16, const void* w_e4m3, const
   // two launches through the workspace: block act-quant, then the GEMM
   const size_t need = fp8_act_quant_gemm_blockscaled_workspace_bytes(M, N, K);
   if (!workspace || workspace_bytes < need) return FP8BS_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return FP8BS_ERR_ALIGN;
   uint8_t* q = static_cast<uint8_t*>(workspace);
   float* sa = reinterpret_cast<float*>(q + round256(M * K));
   uint8_t* gws = q + round256(M * K) + round256(M * (K / kBK) * 4);

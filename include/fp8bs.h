@@ -149,10 +149,14 @@ int fp8_amax_quant_tensor_noalloc(const void* x_bf16, int64_t numel,
  *   w_scale  [N/128, K/128] fp32, 4-byte aligned    (input)
  *   c_bf16   [M, N] bf16, 16-byte aligned           (output, RNE from fp32)
  *   workspace  at least fp8_gemm_blockscaled_workspace_bytes(M, N, K) bytes,
- *              16-byte aligned (NULL allowed when that size is 0, which is
- *              the case unless 32 < M <= 64, N > 2048 and N*K > 2^21); contents on
- *              entry do not matter; not to be shared by calls that can run
- *              concurrently
+ *              16-byte aligned (NULL allowed when that size is 0). K is split
+ *              over several workgroups, with fp32 partial sums in the
+ *              workspace, when 32 < M <= 64, N > 2048 and N*K > 2^21, and
+ *              when M > 64 and the output has fewer than 256 tiles of
+ *              128 x 128 (ceil(M/128) * N/128 < 256), for K >= 4096, or
+ *              K >= 2048 with at most 32 such tiles; the size is 0
+ *              otherwise. Contents on entry do not matter; not to be
+ *              shared by calls that can run concurrently
  * Requires M >= 1, N >= 128, K >= 128, N % 128 == 0, K % 128 == 0,
  * K <= 4194304 (32-bit offsets within a 256-row tile), and K <= 65536 when
  * 32 < M <= 64 and N > 2048 (that path splits K into at most 32 parts).

@@ -99,6 +99,23 @@ def test_ragged_shapes(M, N, K):
     check_full(*operands(a, w, sw), f"ragged {M}x{N}x{K}")
 
 
+# M > 64 with fewer 128 x 128 tiles than CUs and a long enough K: K split
+# over the workgroups, fp32 partials added in split order by a second
+# kernel. Splits of 1 block (M = 96, K = 2048: 16 splits), uneven last splits
+# (K = 56 blocks in 14 splits of 4; 37 blocks), ragged M with a partial
+# 16-row group (1000, 129, 300), the largest M that still splits at N = 2048
+# (1024: 2 splits)
+@pytest.mark.parametrize("M,N,K", [(65, 2048, 7168), (128, 2048, 7168), (96, 256, 2048), (129, 384, 128 * 37),
+                                   (1000, 384, 4096), (1024, 2048, 4096), (300, 1024, 2048)])
+def test_tiled_split_k(M, N, K):
+    fb = binding()
+    assert fb.fp8_gemm_blockscaled_workspace_bytes(M, N, K) > 0
+    rng = np.random.default_rng(M * 3 + N + K)
+    a = synth.f64_to_bf16_bits(rng.standard_normal((M, K)) * 3)
+    w = synth.f64_to_bf16_bits(rng.standard_normal((N, K)) * 0.02)
+    check_full(*operands(a, w), f"split-K {M}x{N}x{K}")
+
+
 INT_CODES = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48}
 
 
@@ -279,15 +296,24 @@ def test_decode_shapes(M, N, K):
     check_full(*operands(a, w), f"decode {M}x{N}x{K}")
 
 
-def test_gemm_workspace_size_and_reuse():
+def test_gemm_workspace_sizes():
     fb = binding()
-    for M in (1, 8, 16, 32, 33, 64, 65, 4096):
+    for M in (1, 8, 16, 32, 33, 64, 4096):
         assert fb.fp8_gemm_blockscaled_workspace_bytes(M, 2048, 7168) == 0
-    # the split-K kernel (32 < M <= 64, N > 2048)
-    M, N, K = 48, 4096, 2048
+    # M > 64 with fewer 128 x 128 tiles than CUs: K split, fp32 partials
+    for M in (65, 128, 1024):
+        assert fb.fp8_gemm_blockscaled_workspace_bytes(M, 2048, 7168) > 0
+
+
+# the split-K decode kernel (32 < M <= 64, N > 2048) and the tiled kernel with
+# K split (M > 64, few tiles): fp32 partials, one [M, N] per K split, in a
+# workspace whose contents on entry do not matter
+@pytest.mark.parametrize("M,N,K", [(48, 4096, 2048), (130, 2048, 2048)])
+def test_gemm_workspace_reuse(M, N, K):
+    fb = binding()
     wsb = fb.fp8_gemm_blockscaled_workspace_bytes(M, N, K)
-    assert wsb >= M * N * 4 and wsb % (M * N * 4) == 0    # fp32 partials, one [M, N] per K split
-    rng = np.random.default_rng(4096)
+    assert wsb >= 2 * M * N * 4 and wsb % (M * N * 4) == 0
+    rng = np.random.default_rng(N + M)
     qa, sa, qw, sw = operands(synth.f64_to_bf16_bits(rng.standard_normal((M, K)) * 3),
                               synth.f64_to_bf16_bits(rng.standard_normal((N, K)) * 0.02))
     args = (u8_to_dev(qa), f32_to_dev(sa), u8_to_dev(qw), f32_to_dev(sw))
@@ -299,12 +325,12 @@ def test_gemm_workspace_size_and_reuse():
     c3 = fb.fp8_gemm_blockscaled(*args, workspace=ws_seq)
     torch.cuda.synchronize()
     assert torch.equal(c1, c2) and torch.equal(c1, c3)
-    check_full(qa, sa, qw, sw, "decode 48x4096x2048 through a reused workspace", c=to_bf16_bits(c2))
+    check_full(qa, sa, qw, sw, f"{M}x{N}x{K} through a reused workspace", c=to_bf16_bits(c2))
     with pytest.raises(fb.Fp8bsError):
         fb.fp8_gemm_blockscaled(*args, workspace=ws[: wsb - 4])
 
 
-@pytest.mark.parametrize("M", [1, 5, 8, 12, 16, 24, 32, 40, 64])
+@pytest.mark.parametrize("M", [1, 5, 8, 12, 16, 24, 32, 40, 64, 128])
 def test_decode_paths_are_deterministic(M):
     # the decode kernels add their partial sums in a fixed order (waves, K
     # block groups, K splits), so repeated calls give identical bits

@@ -92,7 +92,7 @@ def gemm_inputs(fb, M, N, K, r, quant=None):
 
 # decode M = 1 (packed K blocks), 12, 40 and 64 at N = 2048 (chunked full-K
 # kernel), 40 and 64 at N = 4096 (split-K with the reduce kernel); M = 300
-# and 2048 (tiled kernel)
+# (tiled kernel with K split, and its reduce) and 2048 (tiled kernel)
 @pytest.mark.parametrize("M,N,K", [(1, 2048, 7168), (12, 2048, 7168), (40, 2048, 7168), (64, 2048, 7168),
                                    (40, 4096, 2048), (64, 4096, 7168), (300, 1024, 2048), (2048, 2048, 2048)])
 def test_gemm_blockscaled(M, N, K):

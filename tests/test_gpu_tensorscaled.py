@@ -31,7 +31,7 @@ def tensor_operands(a_bits, w_bits):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 2048, 7168), (16, 512, 1024), (4, 128, 128 * 400), (64, 2048, 2048), (33, 256, 640),
-                                   (64, 2048, 7168), (48, 4096, 1024),
+                                   (64, 2048, 7168), (48, 4096, 1024), (128, 2048, 2048), (300, 384, 2048),
                                    (24, 2048, 7168), (30, 256, 128 * 5),
                                    (96, 256, 512), (300, 384, 1024), (1000, 1024, 2048)])
 def test_shapes(M, N, K):

@@ -102,7 +102,8 @@ def check(qa, sa, qw, sw, label):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 2048, 7168), (32, 512, 512), (64, 256, 2048), (12, 256, 128 * 9),
-                                   (24, 384, 2048), (48, 2048, 7168), (40, 2304, 1280),
+                                   (24, 384, 2048), (48, 2048, 7168), (40, 2304, 1280), (128, 2048, 2048),
+                                   (300, 384, 2048),
                                    (96, 256, 512), (300, 384, 1024), (520, 640, 4096),
                                    (300, 384, 2432)])
 def test_gemm_shapes(M, N, K):
