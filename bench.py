@@ -504,7 +504,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "this build has no multi-GPU path.", file=sys.stderr)
+              "the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
