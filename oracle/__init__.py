@@ -11,7 +11,8 @@ Modules
 ``e4m3``  the OCP e4m3 ("fn") format: decode table and round-to-nearest-even
           encoder, from the bit layout (1 sign, 4 exponent, 3 mantissa bits).
 ``quant`` 1x128 block dynamic activation quantization, the per-tensor variant
-          and the 128x128 weight block quantization.
+          (and its apply step with a given scale) and the 128x128 weight
+          block quantization.
 ``gemm``  the fp64 reference of the block-scaled GEMM over dequantized
           operands, and the comparison rules used against the HIP output.
 

@@ -126,6 +126,26 @@ def amax_quant_tensor(x_bits: np.ndarray):
     return q.reshape(x_bits.shape), np.float32(s[0])
 
 
+def static_quant_tensor(x_bits: np.ndarray, scale) -> np.ndarray:
+    """Per-tensor quantization of a bf16 tensor with a given scale.
+
+    The apply-only step of the per-tensor quantizer (TensorRT-LLM PR "Size
+    the per-tensor FP8 dynamic-quant amax grid to the input", sections
+    "Description" and "Correctness": the dynamic op keeps the existing
+    quantize-with-a-scale op, whose bytes the dynamic op must reproduce):
+        q[i] = e4m3(clamp(fl32(x[i] / s), -448, 448))
+    with s the given float32 scale, and, as for a group whose amax is 0, all
+    codes 0x00 when s = 0. Scales that are negative or not finite are outside
+    the contract. Returns uint8 codes of x's shape.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    s = np.float32(scale)
+    if s == 0:
+        return np.zeros(x_bits.shape, dtype=np.uint8)
+    y = (bf16_to_f32(x_bits) / s).astype(np.float32)   # IEEE fp32 division
+    return e4m3.encode(np.clip(y, -F448, F448))
+
+
 def weight_quant_block(w_bits: np.ndarray, block: int = 128):
     """128x128 block quantization of a bf16 [N, K] weight.
 

@@ -401,3 +401,84 @@ def test_f32_input_full_precision_matters():
     q, s = quant.act_quant_block_f32(x)
     assert s[0, 0] == 1.0
     assert q[0, 1] == 0x39 and q[0, 2] == 0x38
+
+
+# --------------------------------------------------------------------------
+# per-tensor quantization with a given (static) scale
+
+def test_static_quant_fraction_bruteforce():
+    # exact rationals: each code is the e4m3 value nearest to the binary32
+    # value nearest to x / s, for scales that are not of the form amax/448,
+    # including one below 2^-64 and quotients that saturate or underflow
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal(96) * np.logspace(-6, 3, 96)
+    x[::7] *= -1
+    x[5] = 0.0
+    bits = synth.f64_to_bf16_bits(x)
+    bits[6] = 0x8000                                    # -0 keeps its sign
+    for s in (np.float32(0.0123), np.float32(1.0), np.float32(3.0e-3), np.float32(2.5),
+              np.float32(7.0e-21), np.float32(6.1e-5)):
+        q = quant.static_quant_tensor(bits, s)
+        assert q.dtype == np.uint8 and q.shape == bits.shape
+        sf = Fraction(float(s))
+        want = [nearest_e4m3(fl32(bf16_value(b) / sf), negative=bool(int(b) & 0x8000)) for b in bits]
+        assert list(q) == want, float(s)
+
+
+def test_static_quant_reproduces_dynamic_codes():
+    # given the dynamic scale, the static op returns the dynamic op's bytes
+    # (the correctness statement of the per-tensor page)
+    for seed, shape, mult in ((3, (4, 2048), 1.0), (4, (1, 2048), 1e-4), (5, (7, 130), 3e2)):
+        x = np.random.default_rng(seed).standard_normal(shape) * mult
+        bits = synth.f64_to_bf16_bits(x)
+        q, s = quant.amax_quant_tensor(bits)
+        assert np.array_equal(quant.static_quant_tensor(bits, s), q)
+    zero = np.zeros((3, 64), np.uint16)
+    q, s = quant.amax_quant_tensor(zero)
+    assert s == 0 and np.array_equal(quant.static_quant_tensor(zero, s), q)
+
+
+def test_static_quant_known_answers():
+    # e4m3 grid values times 2^j quantized with s = 2^j give back their own
+    # codes; past 448 * s the codes saturate to +-448; a zero scale gives 0x00
+    j = -5
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = e4m3.DECODE[codes].astype(np.float64) * 2.0 ** j
+    bits = synth.f64_to_bf16_bits(vals)
+    assert np.array_equal(widen(bits).astype(np.float64), vals)   # exact in bf16
+    q = quant.static_quant_tensor(bits, np.float32(2.0 ** j))
+    want = codes.copy()
+    want[codes == 0x80] = 0x80
+    assert np.array_equal(q, want)
+    big = synth.f64_to_bf16_bits(np.array([1e3, -1e3, 449.0, -460.0, 1e-9, -1e-9]))
+    assert list(quant.static_quant_tensor(big, np.float32(1.0))) == [0x7E, 0xFE, 0x7E, 0xFE, 0x00, 0x80]
+    assert np.all(quant.static_quant_tensor(big, np.float32(0.0)) == 0)
+
+
+def test_static_quant_near_e4m3_midpoints():
+    # scales for which x / s lands within a few binary32 steps of a midpoint
+    # between two e4m3 values: there the binary32 rounding of the quotient
+    # decides the code (multiplying by a rounded reciprocal, or rounding the
+    # exact quotient straight to e4m3, gives a different code in some cases).
+    # Reference: the binary32 quotient from a float64 division (correctly
+    # rounded, 53 >= 2*24 + 2), then the nearest search over the code table.
+    xb = np.arange(0x3F80, 0x4000, dtype=np.uint16)            # bf16 in [1, 2)
+    xb = np.concatenate([xb, xb | 0x8000])
+    xf = widen(xb).astype(np.float64)
+    pos = e4m3.DECODE[:0x7F].astype(np.float64)
+    mids = (pos[0x30:0x48] + pos[0x31:0x49]) / 2
+    rng = np.random.default_rng(23)
+    checked = 0
+    for x0 in rng.choice(xf[:128], 24, replace=False):
+        for t in mids:
+            s0 = np.float32(x0 / t)
+            for k in range(-2, 3):
+                s = s0
+                for _ in range(abs(k)):
+                    s = np.nextafter(s, np.float32(np.inf if k > 0 else 0), dtype=np.float32)
+                q = quant.static_quant_tensor(xb, s)
+                y = (xf / np.float64(s)).astype(np.float32)
+                want = nearest_code_vec(np.clip(y, -F448, F448))
+                assert np.array_equal(q, want), (float(x0), float(t), k)
+                checked += 1
+    assert checked == 24 * len(mids) * 5
