@@ -146,6 +146,12 @@ class Workload:
             self.extra.append(("amax_tensor",
                                lambda i: fb.fp8_amax_tensor(xs[i % rot], out=(amax, sa_only), workspace=ws),
                                2 * numel + 8, 0))
+            # the apply step alone, with the dynamic op's scale given (on the device)
+            fb.fp8_amax_quant_tensor(x, out=(q, s), workspace=ws)
+            s_given = s.clone()
+            self.extra.append(("static_quant_tensor",
+                               lambda i: fb.fp8_static_quant_tensor(xs[i % rot], s_given, out=q),
+                               3 * numel + 4, 0))
             self.config = {"workload": f"per-tensor dynamic quant, X bf16 [{M}, {K}]", "M": M, "K": K}
             self.M, self.N, self.K = M, 0, K
             self.cpu = ("c2", M, K, None)

@@ -34,6 +34,7 @@ __all__ = [
     "fp8_amax_quant_tensor_workspace_bytes",
     "fp8_amax_quant_tensor_noalloc",
     "fp8_amax_tensor",
+    "fp8_static_quant_tensor",
     "fp8_gemm_blockscaled",
     "fp8_gemm_blockscaled_workspace_bytes",
     "fp8_weight_quant_block",
@@ -61,6 +62,7 @@ EXPORTED_SYMBOLS = (
     "fp8_amax_quant_tensor",
     "fp8_amax_quant_tensor_noalloc",
     "fp8_amax_tensor",
+    "fp8_static_quant_tensor",
     "fp8_gemm_blockscaled_workspace_bytes",
     "fp8_gemm_blockscaled",
     "fp8_weight_quant_block",
@@ -114,6 +116,8 @@ def lib() -> ctypes.CDLL:
     L.fp8_amax_quant_tensor_noalloc.restype = ctypes.c_int
     L.fp8_amax_tensor.argtypes = [vp, i64, fp, fp, vp, sz, vp]
     L.fp8_amax_tensor.restype = ctypes.c_int
+    L.fp8_static_quant_tensor.argtypes = [vp, i64, fp, vp, vp]
+    L.fp8_static_quant_tensor.restype = ctypes.c_int
     L.fp8_gemm_blockscaled_workspace_bytes.argtypes = [i64, i64, i64]
     L.fp8_gemm_blockscaled_workspace_bytes.restype = sz
     L.fp8_gemm_blockscaled.argtypes = [vp, fp, vp, fp, vp, i64, i64, i64, vp, sz, vp]
@@ -289,6 +293,25 @@ def fp8_amax_tensor(x: torch.Tensor, out=None, workspace=None):
                                    ctypes.c_void_p(_stream(x.device)))
     _check("fp8_amax_tensor", rc)
     return amax, s
+
+
+def fp8_static_quant_tensor(x: torch.Tensor, scale: torch.Tensor, out=None):
+    """Quantization of bf16 ``x`` (any shape) with a given scale: ``scale`` is
+    a float32 tensor of one element on x's device (read by the kernel).
+    Returns the e4m3 codes."""
+    _need(x, "x", torch.bfloat16)
+    _need(scale, "scale", torch.float32, x.device)
+    if scale.numel() != 1:
+        raise ValueError(f"scale must hold one element, got {scale.numel()}")
+    if out is None:
+        q = torch.empty(x.shape, dtype=E4M3, device=x.device)
+    else:
+        q = _out(out, "q", _CODES, x.shape, x.device)
+    with torch.cuda.device(x.device):
+        rc = lib().fp8_static_quant_tensor(_ptr(x), x.numel(), _ptr(scale), _ptr(q),
+                                           ctypes.c_void_p(_stream(x.device)))
+    _check("fp8_static_quant_tensor", rc)
+    return q
 
 
 def fp8_amax_quant_tensor_noalloc(x: torch.Tensor, out=None):

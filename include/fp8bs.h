@@ -133,6 +133,27 @@ int fp8_amax_quant_tensor_noalloc(const void* x_bf16, int64_t numel,
                                   void* q_e4m3, float* scale, void* stream);
 
 /*
+ * Per-tensor quantization with a given scale: the apply-only quantize op
+ * that the dynamic per-tensor op keeps (TensorRT-LLM PR "Size the per-tensor
+ * FP8 dynamic-quant amax grid to the input", sections "Description" and
+ * "Correctness": the dynamic op's bytes must match this op's for the scale it
+ * computes):
+ *     q[i] = e4m3(clamp(fl32(x[i] / scale[0]), -448, 448))    (IEEE division)
+ * and all codes 0x00 when scale[0] = 0 (the dynamic op's reading for an
+ * all-zero tensor). Given the scale fp8_amax_quant_tensor wrote, the codes
+ * equal that call's, bit for bit.
+ *   x_bf16  [numel] bf16, 16-byte aligned (input)
+ *   scale   ONE fp32 on the device, 4-byte aligned (input, read by the
+ *           kernel: a scale computed on the device needs no host copy);
+ *           a negative or non-finite scale is outside the contract
+ *   q_e4m3  [numel] e4m3, 16-byte aligned (output)
+ * Requires 1 <= numel < 2^42. No workspace. Errors: FP8BS_ERR_NULL,
+ * FP8BS_ERR_SHAPE, FP8BS_ERR_ALIGN, returned before any launch.
+ */
+int fp8_static_quant_tensor(const void* x_bf16, int64_t numel, const float* scale,
+                            void* q_e4m3, void* stream);
+
+/*
  * Block-scaled FP8 GEMM with bf16 output: C = A . W^T.
  * DeepSeek-V3 fp8_gemm_kernel ("How to Profile DeepSeek-V3 Inference Kernels
  * Using Triton Autotuning", sections "Understanding the Autotuned Kernels in

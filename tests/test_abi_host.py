@@ -95,6 +95,20 @@ def test_tensor_quant_noalloc_argument_errors(L):
     assert f(P, 10, P, P + 2, None) == EALIGN
 
 
+def test_static_quant_argument_errors(L):
+    f = L.fp8_static_quant_tensor
+    assert f(None, 10, P, P, None) == ENULL
+    assert f(P, 10, None, P, None) == ENULL
+    assert f(P, 10, P, None, None) == ENULL
+    assert f(P, 0, P, P, None) == ESHAPE
+    assert f(P, -3, P, P, None) == ESHAPE
+    assert f(P, 1 << 42, P, P, None) == ESHAPE
+    assert f(PU, 10, P, P, None) == EALIGN
+    assert f(P, 10, P + 2, P, None) == EALIGN
+    assert f(P, 10, P, P + 8, None) == EALIGN
+    assert f(P, 10, P, P, None) == EDEV          # valid: the device check comes next
+
+
 def test_gemm_argument_errors(L):
     f = L.fp8_gemm_blockscaled
     assert f(None, P, P, P, P, 4, 128, 128, None, 0, None) == ENULL
