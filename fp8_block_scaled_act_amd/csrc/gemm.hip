@@ -98,6 +98,13 @@ __device__ __forceinline__ void copy16_buf_to_lds(uint32_t voff, v4i_rsrc rsrc, 
                "s"(lds_base)
                : "memory", "m0");
 }
+// The same with the non-temporal hint, for data that no other workgroup
+// reads again from the caches (streamed weight rows)
+__device__ __forceinline__ void copy16_buf_to_lds_nt(uint32_t voff, v4i_rsrc rsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rsrc),
+               "s"(lds_base)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void copy4_buf_to_lds(uint32_t voff, v4i_rsrc rsrc, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
                "s"(lds_base)
@@ -1349,7 +1356,12 @@ __global__ __launch_bounds__(64 * kFullWaves) void gemm_blockscaled_decode_full_
         const int r = 8 * (idx % (NR / 8)) + (lane >> 3);
         const uint32_t off = static_cast<uint32_t>(r * K) + static_cast<uint32_t>(c * CB + cb) * kBK +
                              static_cast<uint32_t>(((lane & 7) ^ swz(r)) << 4);
-        copy16_buf_to_lds(off, wr, base + F::kAChunk + idx * 1024);
+        // non-temporal: W rows are streamed, A rows are read by every
+        // workgroup of the group (N = 2048, K = 7168, alternating runs:
+        // M = 16 / 32 / 64 from 7.3 / 8.1-8.2 / 10.0-10.1 to 7.0-7.1 / 7.9-8.0 /
+        // 9.8-9.9 us; the sc0 or sc1 bits besides nt made no difference, sc1
+        // alone none at all)
+        copy16_buf_to_lds_nt(off, wr, base + F::kAChunk + idx * 1024);
       } else if (k < kACopies + kWCopies + kSCopies) {
         if constexpr (SC16) {
           const int r = (4 * lane) / CB, x = (4 * lane) % CB;
