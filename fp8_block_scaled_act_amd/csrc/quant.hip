@@ -20,6 +20,14 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// A load that marks its cache lines as streamed (read once), for inputs that
+// no later pass of the same call reads again.
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---------------------------------------------------------------------------
 // 1x128 blocks. Eight lanes own one block: lane `sub` holds elements
 // [8*sub, 8*sub+8) and [64+8*sub, 64+8*sub+8), so each 16-byte load
@@ -59,8 +67,12 @@ __global__ __launch_bounds__(kThreads) void act_quant_block_kernel(
   const int sub = threadIdx.x & 7;
   if (blk >= nblocks) return;  // whole 8-lane groups leave together
 
-  const uint4 v0 = x[blk * 16 + sub];
-  const uint4 v1 = x[blk * 16 + 8 + sub];
+  // streamed loads: x is read once (rotated inputs, alternating runs: prefill
+  // 17.4-18.0 -> 16.2 us, large-M 19.3 -> 18.1-18.2 us; the same loads in the
+  // float32-input kernel, and in the block kernel of the one-call block and
+  // per-tensor quant, whose second pass re-reads x, were slower)
+  const uint4 v0 = load_nt(x + blk * 16 + sub);
+  const uint4 v1 = load_nt(x + blk * 16 + 8 + sub);
 
   float s;
   uint2 o0, o1;
@@ -212,16 +224,6 @@ constexpr int kVecDeep = 8;
 // each iteration's loads; amax and apply passes over 256 MiB: 113.4 us with
 // 2 in flight, 114.9 with 4)
 constexpr int kApplyVec = 2;
-
-// A load that marks its cache lines as streamed (read once). The amax stage
-// alone uses it (45.4 against 47.8 us over 256 MiB); the quantization's first
-// pass does not, because its second pass re-reads the tensor and finds part
-// of it in the last-level cache only if the first pass left it there.
-typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load_nt(const uint4* p) {
-  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 __device__ __forceinline__ float tail_absmax(const uint16_t* x, int64_t begin, int64_t end, float m) {
   for (int64_t i = begin; i < end; ++i)
@@ -393,6 +395,10 @@ __global__ __launch_bounds__(kSmallThreads) void tensor_quant_mid_kernel(
   if (head) scale[0] = s;
 }
 
+// kStream: streamed loads, for the amax stage alone (45.4 against 47.8 us
+// over 256 MiB); the quantization's first pass does not stream, because its
+// second pass re-reads the tensor and finds part of it in the last-level
+// cache only if the first pass left it there.
 template <bool kStream, int kVec>
 __global__ __launch_bounds__(kThreads) void tensor_amax_partial_kernel(
     const uint16_t* __restrict__ x, float* __restrict__ partial, int64_t numel) {
