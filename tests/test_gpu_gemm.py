@@ -83,6 +83,23 @@ def test_large_tiles_ragged_k_blocks():
     check_full(*operands(a, w), f"{M}x{N}x{K}")
 
 
+def test_large_tiles_ragged_n_and_m():
+    # 256 x 256 tiles (17 x 17 of them fill the chip), N = 33 * 128 and
+    # M = 4100: the last n tile and the last m tile are partial, so the
+    # non-temporal C stores of both edge tiles take the range guard
+    M, N, K = 4100, 33 * 128, 512
+    rng = np.random.default_rng(4224)
+    a = synth.f64_to_bf16_bits(rng.standard_normal((M, K)))
+    w = synth.f64_to_bf16_bits(rng.standard_normal((N, K)) * 0.02)
+    fb = binding()
+    qa, sa, qw, sw = operands(a, w)
+    say("gemm_blockscaled ragged N", (M, N, K))
+    out = torch.full((M, N), -7.0, dtype=torch.bfloat16, device="cuda:0")   # every element must be written
+    fb.fp8_gemm_blockscaled(u8_to_dev(qa), f32_to_dev(sa), u8_to_dev(qw), f32_to_dev(sw), out=out)
+    torch.cuda.synchronize()
+    check_full(qa, sa, qw, sw, f"{M}x{N}x{K}", c=to_bf16_bits(out))
+
+
 def test_c5_large_m():
     d = synth.gen_c5()
     check_full(*operands(d["a"], d["w"], d["w_scale"]), "C5 16384x7168x2048")
