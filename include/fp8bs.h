@@ -7,7 +7,9 @@
  * validates its arguments and enqueues kernels on ``stream``; it never
  * allocates, frees or synchronizes, and outputs are valid once the stream has
  * reached the work. The library keeps no mutable state besides a per-device
- * cache of the device check, so calls from several host threads are safe.
+ * cache of the device check (and the scratch array of
+ * fp8_amax_quant_tensor_noalloc, whose calls must not overlap on one GPU), so
+ * calls from several host threads are safe.
  *
  * Ownership: the caller owns every buffer (inputs, outputs and workspaces).
  * Inputs are read only. Outputs are overwritten entirely and must not alias
