@@ -1156,10 +1156,16 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= mn4) return;
   const float4* p = reinterpret_cast<const float4*>(ws) + i;
-  float4 v[kDecMaxSplits];                 // all loads in flight, then added in split order
+  // all loads in flight, then added in split order; the loads are streamed
+  // (each partial is read once: N = 2048, K = 7168, M = 128 split-K GEMM and
+  // reduce 16.5 -> 14.9 us, M = 256 / 512 unchanged)
+  float4 v[kDecMaxSplits];
 #pragma unroll
   for (int k = 0; k < kDecMaxSplits; ++k)
-    if (k < splits) v[k] = p[k * mn4];
+    if (k < splits) {
+      const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p + k * mn4));
+      v[k] = make_float4(t[0], t[1], t[2], t[3]);
+    }
   float4 s = v[0];
 #pragma unroll
   for (int k = 1; k < kDecMaxSplits; ++k)
