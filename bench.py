@@ -78,8 +78,10 @@ def src_hash(name):
 
 
 def load_traffic(kernel_key, src):
-    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
-    the kernel source changed since they were taken."""
+    """Bytes per launch between the L2 and the memory fabric (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain copy's readings) from committed rocprofv3
+    counter runs: what HBM or the last-level cache served, an upper bound on
+    HBM bytes. None if the kernel source changed since they were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             d = json.load(f)
