@@ -33,8 +33,8 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 128;     // K block
 // m tiles walked per n tile (tile order): 4 for the 256 x 256 tiles, whose
-// C stores are non-temporal, else 8. Large-M (16384 x 7168 x 2048), the same
-// box, alternating: 8 m tiles with cached C stores 227-234 us, 4 with cached
+// C stores are non-temporal, else 8. Large-M (16384 x 7168 x 2048), one GPU,
+// alternating runs: 8 m tiles with cached C stores 227-234 us, 4 with cached
 // stores 229 us, 8 with non-temporal stores 230 us, 4 with non-temporal
 // stores 222-228 us (2 and 16: 224-226 and 227-230 us); prefill unchanged.
 // The L2 fills per launch stay the same (about 181 MiB), so the gain is not
